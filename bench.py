@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Throughput of the exact blockwise attention forward on one MI355X.
+
+One step = one attn_fwd call over the whole workload (default: the LLaMA-7B-shaped
+causal case, B=2 H=32 N=8192 d=128 bf16), inputs already resident in HBM.
+Prints one JSON line: TFLOP/s of counted FLOPs (4 B H N^2 d dense, halved for
+causal, band pairs for the window), the roofline position of the kernel and the
+CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, d=128 N=8192 causal"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense bf16 MFMA; fp32 vector
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["exact_blockwise_attention_attn_amd/csrc/attn_fwd_bf16.hip",
+                  "exact_blockwise_attention_attn_amd/csrc/attn_fwd_f32.hip"]
+
+
+def counted_flops(B, H, N, d, mask, window=0):
+    """4 B H N^2 d for no mask, half of it for causal, 4 B H d x (pairs in the band)
+    for the window |i - j| <= w."""
+    if mask == "none":
+        return 4 * B * H * N * N * d
+    if mask == "causal":
+        return 2 * B * H * N * N * d
+    w = min(window, N - 1)
+    return 4 * B * H * d * (N * (2 * w + 1) - w * (w + 1))
+
+
+def algorithmic_bytes(B, H, N, d, eb):
+    """Read Q, K, V once, write O once and LSE once."""
+    return 4 * B * H * N * d * eb + 4 * B * H * N
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed counter runs, only if they were
+    taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE, encoding="utf-8") as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(workload)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, q, k, v, budget_s=20.0):
+    """The oracle, untuned, on a bounded sample of the workload: whole heads, a
+    seeded subset of query rows, growing until about ``budget_s`` of CPU time."""
+    from oracle.attention_ref import attention_forward
+    from exact_blockwise_attention_attn_amd.inputs import sample_rows
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    rows = sample_rows(wl.N, min(wl.N, 1024), seed=12345, window=wl.window)
+    mk = wl.mask_kind
+    flops = 0
+    heads = 0
+    elapsed = 0.0
+    BH = wl.B * wl.H
+    while heads < BH and elapsed < budget_s:
+        b, h = divmod(heads, wl.H)
+        qn = q[b:b + 1, h:h + 1].float().cpu().numpy()
+        kn = k[b:b + 1, h:h + 1].float().cpu().numpy()
+        vn = v[b:b + 1, h:h + 1].float().cpu().numpy()
+        ts = time.perf_counter()
+        attention_forward(qn, kn, vn, wl.softmax_scale, mk, wl.window, rows=rows)
+        elapsed += time.perf_counter() - ts
+        heads += 1
+        if mk == 0:
+            pairs = len(rows) * wl.N
+        elif mk == 1:
+            pairs = int(np.sum(rows + 1))
+        else:
+            w = min(wl.window, wl.N - 1)
+            pairs = int(np.sum(np.minimum(rows + w, wl.N - 1) - np.maximum(rows - w, 0) + 1))
+        flops += 4 * wl.d * pairs
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {BH} (b,h) heads x {len(rows)} seeded query rows each "
+                      f"(N={wl.N}, d={wl.d}, {wl.mask}), numpy float64, {elapsed:.1f} s",
+            "seconds": elapsed}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of attention, run a plain device copy of MIB MiB per step (the reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: every (batch, head) is independent, so a multi-GPU run would only "
+              "split the heads; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_blockwise_attention_attn_amd as attn
+    from exact_blockwise_attention_attn_amd.inputs import HEADLINE, WORKLOADS, make_qkv
+
+    name = args.workload or HEADLINE
+    wl = WORKLOADS[name]
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    attn.load()
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                          "launches": args.warmup + args.steps}), flush=True)
+        return
+
+    q, k, v = make_qkv(wl.B, wl.H, wl.N, wl.d, wl.torch_dtype, seed=args.seed, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+    flops = counted_flops(wl.B, wl.H, wl.N, wl.d, wl.mask, wl.window)
+    eb = 2 if wl.dtype == "bf16" else 4
+
+    def step():
+        attn.fwd(q, k, v, mask=wl.mask, window=wl.window, scale=wl.softmax_scale, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = gpu_ms / args.steps
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all(), "non-finite output"
+
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    traffic = measured_traffic(name)
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic: seeded i.i.d. N(0,1) q, k, v drawn on the device",
+        "config": {"workload": name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "mask": wl.mask,
+                   "window": wl.window, "scale": wl.softmax_scale, "flops_per_step": flops,
+                   "pct_of_peak": round(100.0 * tflops / peak, 2), "peak_tflops": peak,
+                   "wall_s_timed_region": round(wall, 4)},
+        "roofline": {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": round(tflops, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes": algorithmic_bytes(wl.B, wl.H, wl.N, wl.d, eb),
+                     "algorithmic_gbs": round(algorithmic_bytes(wl.B, wl.H, wl.N, wl.d, eb)
+                                              / (ms_per_step * 1e-3) / 1e9, 1)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

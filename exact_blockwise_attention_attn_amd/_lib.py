@@ -1,0 +1,116 @@
+"""ctypes binding of libattn.so: the C ABI of include/attn.h, one Python function
+per C symbol with the same name and argument order (marshalling only), plus
+``fwd``, a convenience call taking torch tensors.
+
+Nothing here computes attention.  If the library is not built, every call raises;
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_MASK_NONE, ATTN_MASK_CAUSAL, ATTN_MASK_WINDOW = 0, 1, 2
+ATTN_DTYPE_F32, ATTN_DTYPE_BF16 = 0, 1
+ATTN_OK = 0
+ATTN_ERR_NULL_PTR = -1
+ATTN_ERR_BAD_SHAPE = -2
+ATTN_ERR_UNSUPPORTED_HEAD_DIM = -3
+ATTN_ERR_BAD_MASK = -4
+ATTN_ERR_BAD_DTYPE = -5
+ATTN_ERR_ALIAS = -6
+ATTN_ERR_BAD_SCALE = -7
+ATTN_ERR_MISALIGNED = -8
+ATTN_ERR_HIP = -9
+
+MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL, "window": ATTN_MASK_WINDOW}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"attn error {status}: {msg}")
+        self.status = status
+
+
+def load():
+    """Load libattn.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_blockwise_attention_attn_amd._build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i]
+    lib.attn_check_args.restype = i
+    lib.attn_strerror.argtypes = [i]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_fwd(q, k, v, out, lse, B, H, N, d, scale, mask_kind, window, dtype, stream):
+    """C ``attn_fwd``: pointers as ints, returns the status code."""
+    return load().attn_fwd(q, k, v, out, lse, B, H, N, d, scale, mask_kind, window, dtype, stream)
+
+
+def attn_check_args(q, k, v, out, lse, B, H, N, d, scale, mask_kind, window, dtype):
+    """C ``attn_check_args``: host-only argument check, returns the status code."""
+    return load().attn_check_args(q, k, v, out, lse, B, H, N, d, scale, mask_kind, window, dtype)
+
+
+def attn_strerror(status: int) -> str:
+    return load().attn_strerror(status).decode()
+
+
+def attn_version() -> str:
+    return load().attn_version().decode()
+
+
+def fwd(q, k, v, mask="none", window=0, scale=None, out=None, lse=None, stream=None):
+    """Attention forward on torch device tensors [B, H, N, d] (bf16 or fp32).
+
+    Allocates ``out`` ([B, H, N, d], input dtype) and ``lse`` ([B, H, N], fp32)
+    unless given, enqueues the kernel on ``stream`` (default: torch's current
+    stream) and returns (out, lse).  Raises AttnError on any non-zero status."""
+    import torch
+
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must be [B, H, N, d] tensors of one shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q, k, v must all be bfloat16 or all float32")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    for t in (q, k, v):
+        if not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if scale is None:
+        scale = d ** -0.5
+    mk = MASKS[mask] if isinstance(mask, str) else int(mask)
+    dt = ATTN_DTYPE_BF16 if q.dtype == torch.bfloat16 else ATTN_DTYPE_F32
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      B, H, N, d, float(scale), mk, int(window), dt, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, attn_strerror(st))
+    return out, lse

@@ -1,0 +1,93 @@
+// Host side of the C ABI declared in include/attn.h: argument checks, kernel
+// selection and the launch on the caller's stream.  No allocation, no
+// synchronisation, no state.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "attn_launch.h"
+
+namespace {
+
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+}  // namespace
+
+extern "C" int attn_check_args(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                               int B, int H, int N, int d, float scale, int mask_kind, int window, int dtype) {
+    if (!q || !k || !v || !out || !lse) return ATTN_ERR_NULL_PTR;
+    if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_BAD_DTYPE;
+    if (B <= 0 || H <= 0 || N <= 0) return ATTN_ERR_BAD_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+    const uint64_t bh = (uint64_t)B * (uint64_t)H;
+    const uint64_t rows = bh * (uint64_t)N;
+    // per-head offsets are 32-bit, the workgroup count stays far below the grid limit
+    if ((uint64_t)N * (uint64_t)d >= (1ull << 31) || rows >= (1ull << 31) ||
+        bh * (((uint64_t)N + 63) / 64) > (1ull << 24))
+        return ATTN_ERR_BAD_SHAPE;
+    if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL && mask_kind != ATTN_MASK_WINDOW)
+        return ATTN_ERR_BAD_MASK;
+    if (mask_kind == ATTN_MASK_WINDOW && window < 0) return ATTN_ERR_BAD_MASK;
+    if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(lse))
+        return ATTN_ERR_MISALIGNED;
+    const uint64_t eb = dtype == ATTN_DTYPE_F32 ? 4 : 2;
+    const uint64_t tb = rows * (uint64_t)d * eb;   // bytes of one [B, H, N, d] tensor
+    const uint64_t lb = rows * 4;
+    if (overlaps(out, tb, q, tb) || overlaps(out, tb, k, tb) || overlaps(out, tb, v, tb) ||
+        overlaps(lse, lb, q, tb) || overlaps(lse, lb, k, tb) || overlaps(lse, lb, v, tb) ||
+        overlaps(lse, lb, out, tb))
+        return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int B, int H, int N, int d, float scale, int mask_kind, int window,
+                        int dtype, void* stream) {
+    const int st = attn_check_args(q, k, v, out, lse, B, H, N, d, scale, mask_kind, window, dtype);
+    if (st != ATTN_OK) return st;
+
+    AttnLaunch a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    const double c = std::fabs((double)scale) * 1.4426950408889634074;   // log2(e)
+    a.c_log2 = (float)(c > 1e-30 ? c : 1e-30);
+    a.negate_q = scale < 0.f ? 1 : 0;
+    a.mask_kind = mask_kind;
+    a.window = mask_kind == ATTN_MASK_WINDOW ? (window < N - 1 ? window : N - 1) : 0;
+    a.stream = stream;
+
+    (void)hipGetLastError();   // clear a stale error so the check below sees only this launch
+    if (dtype == ATTN_DTYPE_BF16)
+        attn_launch_bf16(a);
+    else
+        attn_launch_f32(a);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" const char* attn_strerror(int status) {
+    switch (status) {
+        case ATTN_OK: return "success";
+        case ATTN_ERR_NULL_PTR: return "a tensor pointer is NULL";
+        case ATTN_ERR_BAD_SHAPE: return "bad shape: B, H, N must be >= 1 and within the size limits";
+        case ATTN_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (d must be 64 or 128)";
+        case ATTN_ERR_BAD_MASK: return "bad mask: unknown mask kind or negative window";
+        case ATTN_ERR_BAD_DTYPE: return "bad dtype (0 = fp32, 1 = bf16)";
+        case ATTN_ERR_ALIAS: return "out or lse overlaps an input or each other";
+        case ATTN_ERR_BAD_SCALE: return "scale is not finite";
+        case ATTN_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
+        case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
+        default: return "unknown status";
+    }
+}
+
+extern "C" const char* attn_version(void) {
+    return "attn 0.1.0 (gfx950; bf16 v_mfma_f32_32x32x16_bf16, fp32 VALU)";
+}

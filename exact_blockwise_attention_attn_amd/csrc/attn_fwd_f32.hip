@@ -1,0 +1,157 @@
+// Exact blockwise attention forward for fp32 inputs (the small-shape path).
+//
+// Same result as the bf16 matrix-core path (softmax(scale Q K^T) V with masked
+// keys excluded, plus the row log-sum-exp), on the vector ALUs.  Nothing is
+// rounded below fp32: scores and the running maximum are carried in fp64, so the
+// exponent arguments of the weights that matter (those near the maximum) are
+// exact to fp32 even for large scores; probabilities and the V accumulation are
+// fp32.
+//
+// A workgroup owns 64 query rows; each row is owned by D/64 neighbouring lanes
+// holding 64 of its dimensions, whose partial dot products are combined with a
+// lane shuffle.  K/V tiles of 32 keys are staged in LDS (lanes of one half read the
+// same key row: an LDS broadcast) and each row keeps a running maximum and sum,
+// normalising once at the end ("Blockwise Parallel Transformer in PyTorch", the
+// blockwise_attention example and its numerical-stability pitfall; Mosaic
+// long-sequence attention page, §3.2 and §5.1).
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_launch.h"
+
+namespace attn_f32 {
+
+constexpr int ROWS = 64;   // query rows per workgroup
+constexpr int TK = 32;     // keys per LDS tile
+constexpr int DD = 64;     // dimensions per lane
+
+template <int MASK>
+__device__ __forceinline__ bool key_allowed(int qi, int kj, int N, int window) {
+    if (kj >= N) return false;
+    if (MASK == ATTN_MASK_CAUSAL) return kj <= qi;
+    if (MASK == ATTN_MASK_WINDOW) return (qi - kj <= window) && (kj - qi <= window);
+    return true;
+}
+
+template <int D, int MASK>
+__global__ __launch_bounds__(ROWS * (D / DD))
+void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+                float* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqt,
+                float c_log2, int negate_q, int window) {
+    constexpr int SPLIT = D / DD;             // lanes per row
+    constexpr int NT = ROWS * SPLIT;
+    __shared__ __attribute__((aligned(16))) float Ks[TK * D];
+    __shared__ __attribute__((aligned(16))) float Vs[TK * D];
+
+    const int tid = threadIdx.x;
+    const int part = tid % SPLIT;             // which 64 dimensions
+    const int row = tid / SPLIT;
+    const int id = blockIdx.x;
+    const int rank = id / BH;
+    const int bh = id - rank * BH;
+    const int qt = (MASK == ATTN_MASK_CAUSAL) ? (nqt - 1 - rank) : rank;
+    const int q0 = qt * ROWS;
+    const int my_q = q0 + row;
+    const int qrow = min(my_q, N - 1);
+    const size_t head = (size_t)bh * N * D;
+    const int dof = part * DD;
+
+    float q[DD], acc[DD];
+    const float sgn = negate_q ? -1.f : 1.f;
+#pragma unroll
+    for (int c = 0; c < DD; c += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(Q + head + (size_t)qrow * D + dof + c);
+        q[c] = sgn * x.x; q[c + 1] = sgn * x.y; q[c + 2] = sgn * x.z; q[c + 3] = sgn * x.w;
+        acc[c] = acc[c + 1] = acc[c + 2] = acc[c + 3] = 0.f;
+    }
+    double m = -INFINITY;      // running max of c_log2 * s (log2 domain)
+    float l = 0.f;
+
+    const int r1 = min(q0 + ROWS, N) - 1;
+    const int last = (N - 1) / TK;
+    int lo = 0, hi = last;
+    if (MASK == ATTN_MASK_CAUSAL) hi = min(last, r1 / TK);
+    if (MASK == ATTN_MASK_WINDOW) { lo = max(0, q0 - window) / TK; hi = min(N - 1, r1 + window) / TK; }
+    const double c = (double)c_log2;
+
+    for (int t = lo; t <= hi; ++t) {
+        const int key0 = t * TK;
+        for (int e = tid * 4; e < TK * D; e += NT * 4) {
+            const int kr = e / D, col = e % D;
+            float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+            if (key0 + kr < N) {
+                kv = *reinterpret_cast<const float4*>(K + head + (size_t)(key0 + kr) * D + col);
+                vv = *reinterpret_cast<const float4*>(V + head + (size_t)(key0 + kr) * D + col);
+            }
+            *reinterpret_cast<float4*>(Ks + e) = kv;
+            *reinterpret_cast<float4*>(Vs + e) = vv;
+        }
+        __syncthreads();
+
+        double s[TK];
+        double mt = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < TK; ++j) {
+            double dot = 0.0;
+#pragma unroll
+            for (int cc = 0; cc < DD; ++cc) dot = __builtin_fma((double)q[cc], (double)Ks[j * D + dof + cc], dot);
+            if (SPLIT == 2) dot += __shfl_xor(dot, 1);
+            s[j] = key_allowed<MASK>(my_q, key0 + j, N, window) ? dot * c : -INFINITY;
+            mt = fmax(mt, s[j]);
+        }
+        const double m_new = fmax(m, mt);
+        const double base = (m_new == -INFINITY) ? 0.0 : m_new;
+        const float alpha = __builtin_amdgcn_exp2f((float)(m - base));
+        l *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < DD; ++cc) acc[cc] *= alpha;
+#pragma unroll
+        for (int j = 0; j < TK; ++j) {
+            const float p = __builtin_amdgcn_exp2f((float)(s[j] - base));
+            l += p;
+#pragma unroll
+            for (int cc = 0; cc < DD; ++cc) acc[cc] = __builtin_fmaf(p, Vs[j * D + dof + cc], acc[cc]);
+        }
+        m = m_new;
+        __syncthreads();
+    }
+
+    if (my_q < N) {
+        const float inv = 1.0f / l;
+#pragma unroll
+        for (int cc = 0; cc < DD; cc += 4) {
+            float4 y = {acc[cc] * inv, acc[cc + 1] * inv, acc[cc + 2] * inv, acc[cc + 3] * inv};
+            *reinterpret_cast<float4*>(O + head + (size_t)my_q * D + dof + cc) = y;
+        }
+        if (part == 0)
+            LSE[(size_t)bh * N + my_q] =
+                (float)((m + (double)__builtin_amdgcn_logf(l)) * 0.69314718055994530942);
+    }
+}
+
+template <int D, int MASK>
+static int launch(const AttnLaunch& a) {
+    const int nqt = (a.N + ROWS - 1) / ROWS;
+    const long long grid = (long long)nqt * a.B * a.H;
+    hipLaunchKernelGGL((fwd_kernel<D, MASK>), dim3((unsigned)grid), dim3(ROWS * (D / DD)), 0,
+                       (hipStream_t)a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (float*)a.out, a.lse, a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window);
+    return 0;
+}
+
+template <int D>
+static int by_mask(const AttnLaunch& a) {
+    switch (a.mask_kind) {
+        case ATTN_MASK_CAUSAL: return launch<D, ATTN_MASK_CAUSAL>(a);
+        case ATTN_MASK_WINDOW: return launch<D, ATTN_MASK_WINDOW>(a);
+        default: return launch<D, ATTN_MASK_NONE>(a);
+    }
+}
+
+}  // namespace attn_f32
+
+int attn_launch_f32(const AttnLaunch& a) {
+    if (a.d == 128) return attn_f32::by_mask<128>(a);
+    return attn_f32::by_mask<64>(a);
+}

@@ -1,0 +1,21 @@
+// Internal launch descriptor shared by the host entry point and the kernel files.
+#pragma once
+
+#include "../../include/attn.h"
+
+struct AttnLaunch {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;
+    int B, H, N, d;
+    float c_log2;      // |scale| * log2(e), floored at 1e-30 so masked scores stay -inf
+    int negate_q;      // scale < 0: the kernels negate q (exact for bf16/fp32) and use |scale|
+    int mask_kind;
+    int window;        // clamped to [0, N-1]
+    void* stream;
+};
+
+int attn_launch_bf16(const AttnLaunch& a);
+int attn_launch_f32(const AttnLaunch& a);

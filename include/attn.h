@@ -1,0 +1,104 @@
+/*
+ * attn.h - C ABI of the exact blockwise attention forward library (libattn.so).
+ *
+ * The operation.  For every batch b, head h and query row i, with N queries and
+ * N keys per head:
+ *
+ *     s_ij   = scale * <q_i, k_j>             for keys j allowed by the mask
+ *     O_i    = sum_j softmax_j(s_ij) v_j      (masked keys get probability 0)
+ *     LSE_i  = ln sum_j exp(s_ij)             (natural log, allowed keys only)
+ *
+ * This is softmax(Q K^T / sqrt(d_k)) V ("Transformer多头注意力8头并行计算PyTorch实现与
+ * CUDA核函数优化", §1), with masked scores set to -inf before the softmax (same page,
+ * §2.2).  It is computed blockwise: every block of queries walks the keys tile by
+ * tile with a running maximum and sum, so the N x N score matrix never exists
+ * ("Blockwise Parallel Transformer in PyTorch", the blockwise_attention example;
+ * Mosaic long-sequence attention page, §2.2 and §3.2).  LSE is the log-space
+ * statistic that keeps the softmax free of overflow (Mosaic page, §5.1).
+ *
+ * Masks (mask_kind):
+ *     ATTN_MASK_NONE    every key
+ *     ATTN_MASK_CAUSAL  key j allowed iff j <= i (square, top-left aligned)
+ *     ATTN_MASK_WINDOW  key j allowed iff |i - j| <= window, the inclusive band of
+ *                       the sliding-window section ("长序列推理中的注意力机制优化策略与实践",
+ *                       §2.1); clipped at both ends of the sequence.
+ * Every row has at least one allowed key (its own), so O and LSE are always finite
+ * for finite inputs.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_mask_kind { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL = 1, ATTN_MASK_WINDOW = 2 };
+
+enum attn_dtype { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 };
+
+enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL_PTR = -1,              /* a tensor pointer is NULL                        */
+    ATTN_ERR_BAD_SHAPE = -2,             /* B, H or N <= 0, or a size overflows the limits  */
+    ATTN_ERR_UNSUPPORTED_HEAD_DIM = -3,  /* d not in {64, 128}                              */
+    ATTN_ERR_BAD_MASK = -4,              /* unknown mask_kind, or window < 0 for WINDOW     */
+    ATTN_ERR_BAD_DTYPE = -5,             /* dtype not an attn_dtype                         */
+    ATTN_ERR_ALIAS = -6,                 /* out or lse overlaps q, k, v or each other       */
+    ATTN_ERR_BAD_SCALE = -7,             /* scale is NaN or infinite                        */
+    ATTN_ERR_MISALIGNED = -8,            /* a tensor pointer is not 16-byte aligned         */
+    ATTN_ERR_HIP = -9                    /* the HIP runtime reported an error at launch     */
+};
+
+/*
+ * attn_fwd - exact attention forward, O and LSE.
+ *
+ *   q, k, v   device pointers, each a contiguous row-major [B, H, N, d] tensor of
+ *             `dtype` (fp32 or bf16); read only.
+ *   out       device pointer, contiguous [B, H, N, d] of `dtype`; fully overwritten.
+ *   lse       device pointer, contiguous [B, H, N] of fp32; fully overwritten.
+ *   B, H, N   batch, heads, sequence length; each >= 1.  Limits: N * d < 2^31,
+ *             B * H * N < 2^31.
+ *   d         head dimension: 64 or 128.
+ *   scale     softmax scale applied to q.k (1/sqrt(d) for standard attention); finite.
+ *   mask_kind an attn_mask_kind.
+ *   window    band half-width w >= 0; read only when mask_kind == ATTN_MASK_WINDOW.
+ *   dtype     an attn_dtype: the element type of q, k, v and out.  bf16 inputs are
+ *             multiplied on bf16 matrix cores with fp32 accumulation; the
+ *             probabilities are rounded to bf16 for the P.V product; O is rounded
+ *             to bf16 (nearest-even) from fp32.  fp32 inputs are computed in fp32.
+ *   stream    a hipStream_t (NULL = the default stream) on the current device.
+ *
+ * Ownership: the caller allocates and frees all five buffers on the current
+ * device.  The library allocates nothing, frees nothing and never synchronises:
+ * the call enqueues the work on `stream` and returns.  It keeps no state between
+ * calls and may be called concurrently from several host threads.
+ *
+ * Errors: returns ATTN_OK (0) or a negative attn_status.  Argument errors are
+ * detected on the host before anything is enqueued, so nothing is written on such
+ * an error.  ATTN_ERR_HIP means the launch itself failed (hipGetLastError); the
+ * outputs are then undefined.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int H, int N, int d, float scale, int mask_kind, int window,
+             int dtype, void* stream);
+
+/*
+ * attn_check_args - the host-side argument check attn_fwd performs, on its own.
+ * Same arguments as attn_fwd minus the stream; touches no device and no pointer
+ * target (pointers are compared, never dereferenced).  Returns what attn_fwd
+ * would return before launching.
+ */
+int attn_check_args(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                    int B, int H, int N, int d, float scale, int mask_kind, int window, int dtype);
+
+/* attn_strerror - static, NUL-terminated text for a status code (never NULL). */
+const char* attn_strerror(int status);
+
+/* attn_version - static, NUL-terminated library version and target string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,107 @@
+"""Host-only checks of the C ABI: the library loads, exports every function that
+include/attn.h declares, and rejects bad arguments before touching a device.
+No compute call is made (there is no GPU here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_blockwise_attention_attn_amd as attn
+from exact_blockwise_attention_attn_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["attn_check_args", "attn_fwd", "attn_strerror", "attn_version"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_header_enums_match_binding():
+    text = open(HEADER, encoding="utf-8").read()
+    for name, value in re.findall(r"\b(ATTN_[A-Z0-9_]+)\s*=\s*(-?\d+)", text):
+        assert getattr(_lib, name) == int(value), name
+
+
+def test_version_and_strerror():
+    assert "gfx950" in attn.attn_version()
+    for code in range(-9, 1):
+        msg = attn.attn_strerror(code)
+        assert msg and msg != "unknown status"
+    assert attn.attn_strerror(-100) == "unknown status"
+
+
+# A fake but aligned, non-overlapping address layout: nothing is ever dereferenced.
+BASE = 1 << 40
+GAP = 1 << 36
+
+
+def ptrs():
+    return [BASE + i * GAP for i in range(5)]
+
+
+def check(**kw):
+    q, k, v, o, l = ptrs()
+    args = dict(q=q, k=k, v=v, out=o, lse=l, B=2, H=4, N=100, d=128, scale=0.1, mask_kind=0, window=0, dtype=1)
+    args.update(kw)
+    return attn.attn_check_args(args["q"], args["k"], args["v"], args["out"], args["lse"], args["B"], args["H"],
+                                args["N"], args["d"], args["scale"], args["mask_kind"], args["window"], args["dtype"])
+
+
+def test_valid_arguments_pass():
+    assert check() == 0
+    assert check(dtype=0, d=64, mask_kind=2, window=0) == 0
+    assert check(mask_kind=1, scale=-0.5) == 0
+    assert check(scale=0.0) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), _lib.ATTN_ERR_NULL_PTR), (dict(k=0), _lib.ATTN_ERR_NULL_PTR), (dict(v=0), _lib.ATTN_ERR_NULL_PTR),
+    (dict(out=0), _lib.ATTN_ERR_NULL_PTR), (dict(lse=0), _lib.ATTN_ERR_NULL_PTR),
+    (dict(B=0), _lib.ATTN_ERR_BAD_SHAPE), (dict(H=-1), _lib.ATTN_ERR_BAD_SHAPE), (dict(N=0), _lib.ATTN_ERR_BAD_SHAPE),
+    (dict(N=1 << 24, d=128), _lib.ATTN_ERR_BAD_SHAPE),              # N*d = 2^31
+    (dict(B=1 << 16, H=1 << 15, N=1), _lib.ATTN_ERR_BAD_SHAPE),     # B*H*N = 2^31
+    (dict(d=96), _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM), (dict(d=0), _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM),
+    (dict(d=256), _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM),
+    (dict(mask_kind=3), _lib.ATTN_ERR_BAD_MASK), (dict(mask_kind=-1), _lib.ATTN_ERR_BAD_MASK),
+    (dict(mask_kind=2, window=-1), _lib.ATTN_ERR_BAD_MASK),
+    (dict(dtype=2), _lib.ATTN_ERR_BAD_DTYPE),
+    (dict(scale=float("nan")), _lib.ATTN_ERR_BAD_SCALE), (dict(scale=float("inf")), _lib.ATTN_ERR_BAD_SCALE),
+    (dict(q=BASE + 8), _lib.ATTN_ERR_MISALIGNED), (dict(lse=BASE + 4 * GAP + 4), _lib.ATTN_ERR_MISALIGNED),
+    (dict(out=BASE), _lib.ATTN_ERR_ALIAS),                            # out == q
+    (dict(out=BASE + 2 * GAP + 4096), _lib.ATTN_ERR_ALIAS),           # out inside v
+    (dict(lse=BASE + 3 * GAP + 16), _lib.ATTN_ERR_ALIAS),             # lse inside out
+])
+def test_invalid_arguments(kw, code):
+    assert check(**kw) == code
+
+
+def test_window_ignored_unless_window_mask():
+    assert check(mask_kind=0, window=-5) == 0
+    assert check(mask_kind=1, window=-5) == 0
+
+
+def test_fwd_rejects_before_launch():
+    # attn_fwd runs the same checks first and returns without any device call
+    q, k, v, o, l = ptrs()
+    assert attn.attn_fwd(q, k, v, o, l, 1, 1, 8, 96, 0.1, 0, 0, 1, None) == _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM
+    assert attn.attn_fwd(0, k, v, o, l, 1, 1, 8, 64, 0.1, 0, 0, 1, None) == _lib.ATTN_ERR_NULL_PTR
+    assert attn.attn_fwd(q, k, v, q, l, 1, 1, 8, 64, 0.1, 0, 0, 1, None) == _lib.ATTN_ERR_ALIAS
+
+
+def test_binding_names_match_c_symbols():
+    for name in declared_functions():
+        assert callable(getattr(attn, name))

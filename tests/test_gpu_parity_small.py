@@ -1,0 +1,104 @@
+"""GPU parity on small shapes, all rows checked: every mask, both dtypes and head
+dims, ragged lengths around the tile sizes, window widths at tile edges, and the
+degenerate cases (N = 1, w = 0, w >= N - 1, negative and zero scale)."""
+import numpy as np
+import pytest
+import torch
+
+import exact_blockwise_attention_attn_amd as attn
+from tests.gpu_util import compare, oracle, require_gpu, run_case, say, to_np
+from exact_blockwise_attention_attn_amd.inputs import make_qkv
+
+pytestmark = pytest.mark.gpu
+
+RAGGED_N = [1, 2, 17, 63, 64, 65, 127, 128, 129, 300, 1000]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", ["none", "causal"])
+@pytest.mark.parametrize("N", RAGGED_N)
+def test_ragged(dtype, d, mask, N):
+    run_case(1, 2, N, d, dtype, mask, seed=N, name="ragged")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,w", [(300, 0), (300, 1), (300, 63), (300, 64), (300, 65), (300, 299), (300, 5000),
+                                 (1000, 127), (1000, 128), (1000, 200), (129, 31), (1, 0), (2, 1)])
+def test_window(dtype, d, N, w):
+    run_case(1, 2, N, d, dtype, "window", window=w, seed=N + w, name="window")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_batches_and_heads(dtype):
+    run_case(3, 5, 200, 64, dtype, "causal", seed=7, name="bh")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 1e-3, 2.0])
+def test_scale_values(dtype, scale):
+    run_case(1, 2, 160, 64, dtype, "causal", scale=scale, seed=11, name="scale")
+
+
+@pytest.mark.parametrize("q_mult", [8.0, 32.0])
+@pytest.mark.parametrize("mask", ["none", "causal", "window"])
+def test_peaked_rows(q_mult, mask):
+    # large scores: exp overflow without the running max, strong max rescaling
+    run_case(1, 2, 700, 128, "bf16", mask, window=100, seed=3, q_mult=q_mult, name="peaked")
+
+
+def test_zero_query_uniform_average():
+    # Q = 0: O_i is the mean of the allowed V rows, LSE_i = ln |A(i)| (closed form)
+    N, d = 333, 128
+    q = torch.zeros(1, 1, N, d, dtype=torch.bfloat16, device="cuda")
+    _, k, v = make_qkv(1, 1, N, d, torch.bfloat16, seed=5, device="cpu")
+    out, lse = attn.fwd(q, k.cuda(), v.cuda(), mask="causal")
+    torch.cuda.synchronize()
+    vn = to_np(v)[0, 0]
+    ref = np.cumsum(vn, axis=0) / np.arange(1, N + 1)[:, None]
+    assert np.max(np.abs(to_np(out)[0, 0] - ref)) <= 2e-2
+    assert np.max(np.abs(to_np(lse)[0, 0] - np.log(np.arange(1, N + 1)))) <= 1e-3
+
+
+def test_deterministic_and_canary():
+    """Two runs are bitwise equal; every output element is overwritten (NaN canary)."""
+    q, k, v = (t.cuda() for t in make_qkv(2, 4, 1000, 128, torch.bfloat16, seed=21))
+    outs = []
+    for _ in range(2):
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full((2, 4, 1000), float("nan"), device="cuda")
+        attn.fwd(q, k, v, mask="window", window=77, out=out, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all() and torch.isfinite(lse).all()
+        outs.append((out.clone(), lse.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_side_stream():
+    q, k, v = (t.cuda() for t in make_qkv(1, 4, 513, 64, torch.bfloat16, seed=8))
+    ref_o, ref_l = attn.fwd(q, k, v, mask="causal")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o2, l2 = attn.fwd(q, k, v, mask="causal")
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_o, o2) and torch.equal(ref_l, l2)
+
+
+def test_errors_leave_outputs_untouched():
+    q, k, v = (t.cuda() for t in make_qkv(1, 1, 64, 64, torch.bfloat16, seed=1))
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((1, 1, 64), 7.0, device="cuda")
+    with pytest.raises(attn.AttnError):
+        attn.fwd(q, k, v, mask="window", window=-1, out=out, lse=lse)
+    with pytest.raises(attn.AttnError):
+        attn.fwd(q, k, v, scale=float("nan"), out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert (out == 7.0).all() and (lse == 7.0).all()
