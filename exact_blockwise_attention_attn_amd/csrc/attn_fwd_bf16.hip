@@ -11,24 +11,41 @@
 // overflow is the source of NaN; work relative to the maximum, in log space).
 //
 // Work decomposition.  One workgroup per (batch*head, block of BR = 32*NW query
-// rows); wave w of the workgroup owns 32 query rows.  The workgroup walks the key
-// tiles (BC = 64 keys) that hold an allowed key for one of its rows; whole tiles
-// outside the mask are never visited, and element masking runs only on tiles that
-// straddle the mask or the sequence end.
+// rows); wave w owns 32 query rows.  The workgroup walks the key tiles (BC = 64
+// keys) that hold an allowed key for one of its rows; tiles wholly outside the
+// mask are never visited and element masking runs only on tiles that straddle the
+// mask or the sequence end.  A wave skips the matrix work of tiles that hold no
+// allowed key for its own 32 rows.
+//
+// K/V staging.  Each K and V tile goes HBM -> LDS directly (global_load_lds_dwordx4,
+// no VGPR round trip), row-major with the 16-byte chunks of a row XOR-swizzled by
+// the row index, into one of two buffers: tile t+1 streams in while tile t is
+// consumed, one barrier per tile.  The two buffers are distinct LDS arrays and the
+// tile loop is unrolled by two, so every LDS read names its buffer statically and
+// the compiler can see it never aliases the load in flight into the other one.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, 64-wide wavefront).  Each wave
 // computes the transposed score block S^T = K_tile Q_w^T (keys x queries), so a
-// lane holds scores of ONE query (column n = lane % 32) for 32 of the 64 keys; the
-// row max and row sum are in-lane reductions plus one exchange with lane ^ 32
-// (v_permlane32_swap).  The probabilities stay in registers: the C layout of S^T
-// is reused directly as the B operand of O^T += V^T P^T after packing to bf16, with
-// the key order of each 16-key slab permuted identically on the V^T side (a
-// contraction index may be permuted freely).  V^T is stored in LDS transposed and
-// in that permuted key order, so the A operand is one 16-byte LDS read per lane.
+// lane holds scores of ONE query (column n = lane % 32) for 32 of the 64 keys: row
+// max and sums are in-lane plus one exchange with lane ^ 32 (v_permlane32_swap).
+// The probabilities never leave registers: the C layout of S^T, packed to bf16, is
+// the B operand of O^T += V^T P^T, where the 8 keys a lane holds per 16-key slab
+// are {4h..4h+3, 8+4h..8+4h+3} (h = lane / 32); the A operand V^T is read from the
+// row-major V tile with the transposing LDS read ds_read_b64_tr_b16 in exactly
+// that key order (a contraction index may be permuted, as long as both operands
+// agree).
+//
+// Softmax bookkeeping (log2 domain, c = |scale| log2 e): the running maximum is
+// raised only when some row of the wave grows by more than TAU (then the O
+// accumulator and sums are rescaled), so most tiles skip the rescale.  Two sums
+// are kept: the fp32 sum of the probabilities (for LSE) and the sum of the same
+// probabilities rounded to bf16 (v_dot2 with ones), which normalises O: O is then
+// an exact convex combination of V rows with the rounded weights, and the bf16
+// rounding of P perturbs relative weights only.
 //
 // Data in HBM: q, k, v, out are contiguous [B, H, N, d] bf16, lse is [B, H, N] fp32.
-// Q is read once into registers, K and V once per query block (served mostly from
-// L2/MALL), O and LSE written once.
+// Q is read once into registers, K and V once per query block (mostly L2/MALL
+// hits), O and LSE written once.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -39,44 +56,50 @@ namespace attn_bf16 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int BC = 64;              // keys per tile
+
+template <int V>
+struct IntC { static constexpr int value = V; };
 constexpr float TAU = 8.0f;         // lazy rescale threshold (log2 domain)
 
 template <int D, int NW>
 struct Cfg {
-    static constexpr int NT = 64 * NW;          // threads per workgroup
-    static constexpr int BR = 32 * NW;          // query rows per workgroup
-    static constexpr int KST = D + 8;           // K tile row stride (elements), keeps 16 B reads conflict-free
-    static constexpr int VST = BC + 8;          // V^T tile row stride (elements)
-    static constexpr int K_ELEMS = BC * KST;
-    static constexpr int V_ELEMS = D * VST;
-    static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-    static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;       // two buffers of bf16
-    static constexpr int K_CHUNKS = BC * D / 8;               // 16-byte chunks in a K tile
-    static constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
-    static constexpr int V_UNITS = (BC / 4) * (D / 8);        // (4 keys x 8 dims) units of a V tile
-    static constexpr int V_PER_T = (V_UNITS + NT - 1) / NT;
+    static constexpr int NT = 64 * NW;              // threads per workgroup
+    static constexpr int BR = 32 * NW;              // query rows per workgroup
+    static constexpr int CPR = D / 8;               // 16-byte chunks per row
+    static constexpr int TILE_BYTES = BC * D * 2;   // one K or V tile
+    static constexpr int BUF_BYTES = 2 * TILE_BYTES;             // K tile + V tile
+    static constexpr int LDS_BYTES = 2 * BUF_BYTES;              // both buffers
+    static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / NW;  // 1 KB per wave instruction
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CDNA4 workgroup");
-    static_assert(D % 32 == 0, "head dim must be a multiple of 32");
+    static_assert(TILE_BYTES % (1024 * NW) == 0, "tile must split evenly over the waves");
+    static_assert(D == 64 || D == 128, "head dim");
 };
 
-// Position of key k (0..15) of a 16-key slab inside the permuted V^T row: lane half
-// h of the P^T operand holds keys {4h..4h+3, 8+4h..8+4h+3} (the S^T C layout), and
-// those 8 keys must sit contiguously at positions 8h..8h+7.
-__device__ __forceinline__ int slab_pos(int k) {
-    return ((k >> 2) & 1) * 8 + (k >> 3) * 4 + (k & 3);
+// XOR applied to the chunk index of a row.  It makes both LDS read patterns
+// conflict-free on 64 banks: 16 consecutive rows at one chunk (K operand, 16-byte
+// reads) and 4 consecutive rows x 4 consecutive chunks (V operand, transposing
+// 8-byte reads).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-__device__ __forceinline__ float wave_swap32_max(float x) {
+__device__ __forceinline__ float swap32_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__device__ __forceinline__ float wave_swap32_add(float x) {
+__device__ __forceinline__ float swap32_add(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
@@ -105,75 +128,9 @@ __device__ __forceinline__ void tile_range(int r0, int r1, int N, int window, in
     }
 }
 
-template <int D, int NW>
-struct TileRegs {
-    u32x4 k[Cfg<D, NW>::K_PER_T];
-    u32x4 v[Cfg<D, NW>::V_PER_T][4];
-};
-
-template <int D, int NW>
-__device__ __forceinline__ void load_tile(TileRegs<D, NW>& tr, const __bf16* __restrict__ Kh,
-                                          const __bf16* __restrict__ Vh, int key0, int N, int tid) {
-    using C = Cfg<D, NW>;
-    constexpr int CPR = D / 8;                        // 16-byte chunks per row
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-        const int c = tid + i * C::NT;
-        const int row = c / CPR, col = (c % CPR) * 8;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if ((C::K_CHUNKS % C::NT == 0 || c < C::K_CHUNKS) && key0 + row < N)
-            val = *reinterpret_cast<const u32x4*>(Kh + (size_t)(key0 + row) * D + col);
-        tr.k[i] = val;
-    }
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-        const int u = tid + i * C::NT;
-        const int grp = u / CPR, col = (u % CPR) * 8;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int key = key0 + grp * 4 + r;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if ((C::V_UNITS % C::NT == 0 || u < C::V_UNITS) && key < N)
-                val = *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D + col);
-            tr.v[i][r] = val;
-        }
-    }
-}
-
-template <int D, int NW>
-__device__ __forceinline__ void store_tile(const TileRegs<D, NW>& tr, __bf16* Ks, __bf16* Vt, int tid) {
-    using C = Cfg<D, NW>;
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int i = 0; i < C::K_PER_T; ++i) {
-        const int c = tid + i * C::NT;
-        if (C::K_CHUNKS % C::NT == 0 || c < C::K_CHUNKS) {
-            const int row = c / CPR, col = (c % CPR) * 8;
-            *reinterpret_cast<u32x4*>(Ks + row * C::KST + col) = tr.k[i];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < C::V_PER_T; ++i) {
-        const int u = tid + i * C::NT;
-        if (C::V_UNITS % C::NT == 0 || u < C::V_UNITS) {
-            const int grp = u / CPR, col = (u % CPR) * 8;
-            const int key = grp * 4;                                  // first of 4 keys
-            const int pos = (key >> 4) * 16 + slab_pos(key & 15);    // 4 consecutive positions
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // dword w of each row holds dims (col+2w, col+2w+1)
-                const uint32_t a0 = tr.v[i][0][w], a1 = tr.v[i][1][w];
-                const uint32_t a2 = tr.v[i][2][w], a3 = tr.v[i][3][w];
-                const uint32_t lo01 = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-                const uint32_t hi01 = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-                const uint32_t lo23 = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-                const uint32_t hi23 = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-                u32x2 even = {lo01, lo23}, odd = {hi01, hi23};
-                *reinterpret_cast<u32x2*>(Vt + (col + 2 * w) * C::VST + pos) = even;
-                *reinterpret_cast<u32x2*>(Vt + (col + 2 * w + 1) * C::VST + pos) = odd;
-            }
-        }
-    }
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* lds_base, int byte_off) {
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_base + byte_off));
+    return __builtin_bit_cast(bf16x4, r);
 }
 
 template <int D, int NW, int MASK>
@@ -184,11 +141,13 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     using C = Cfg<D, NW>;
     constexpr int NS = D / 16;       // 16-dim slabs of the contraction over d
     constexpr int ND = D / 32;       // 32-row blocks of O^T
-    __shared__ __attribute__((aligned(16))) __bf16 lds[2 * C::BUF_ELEMS];
+    constexpr int CPR = C::CPR;
+    __shared__ __attribute__((aligned(1024))) char lds0[C::BUF_BYTES];
+    __shared__ __attribute__((aligned(1024))) char lds1[C::BUF_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hl = lane >> 5;        // lane half
     const int ln = lane & 31;
 
@@ -219,29 +178,68 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         qreg[s] = __builtin_bit_cast(bf16x8, raw);
     }
 
+    // ---- per-lane LDS addresses (byte offsets within a K or V tile)
+    // loader: wave instruction i fills 1 KB block b = wave * LPW + i; lane -> slot
+    int ld_row[C::LOADS_PER_WAVE], ld_col[C::LOADS_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+        const int slot = (wave * C::LOADS_PER_WAVE + i) * 64 + lane;
+        const int row = slot / CPR;
+        ld_row[i] = row;
+        ld_col[i] = ((slot % CPR) ^ swz<D>(row)) * 8;
+    }
+    // K operand: row ln (and 32 + ln, same swizzle), chunk 2 s + hl
+    int kaddr[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) kaddr[s] = (ln * CPR + ((2 * s + hl) ^ swz<D>(ln))) * 16;
+    // V operand: transposing reads; read r of d-block j, supplier lane (g, s16)
+    int vaddr[2][ND];
+    {
+        const int g = lane >> 4, s16 = lane & 15;
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int j = 0; j < ND; ++j) {
+                const int rr = 8 * r + 4 * hl + (s16 >> 2);                 // key within a 16-key slab
+                const int chunk = 4 * j + 2 * (g & 1) + ((s16 & 3) >> 1);
+                vaddr[r][j] = (rr * CPR + (chunk ^ swz<D>(rr))) * 16 + (s16 & 1) * 8;
+            }
+    }
+
     int t_lo, t_hi;
     tile_range<MASK>(q0, min(q0 + C::BR, N) - 1, N, window, t_lo, t_hi);
     int w_lo = 1, w_hi = 0;                      // this wave's own tile range (empty if no rows)
     if (qw0 < N) tile_range<MASK>(qw0, min(qw0 + 31, N - 1), N, window, w_lo, w_hi);
+
+    // issue the direct HBM -> LDS loads of key tile t into buffer `kb`
+    auto load_tile = [&](int t, char* kb) {
+        const int key0 = t * BC;
+        char* vb = kb + C::TILE_BYTES;
+#pragma unroll
+        for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+            const int row = min(key0 + ld_row[i], N - 1);       // rows past the end: any valid row, masked later
+            const size_t off = (size_t)row * D + ld_col[i];
+            const int blk = (wave * C::LOADS_PER_WAVE + i) * 1024;
+            __builtin_amdgcn_global_load_lds((const void*)(Kh + off), (lds_void*)(kb + blk), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(Vh + off), (lds_void*)(vb + blk), 16, 0, 0);
+        }
+    };
 
     f32x16 o[ND];
 #pragma unroll
     for (int j = 0; j < ND; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
-    float m_run = -INFINITY;     // running max of c_log2 * s (log2 domain), lazily updated
-    float l_run = 0.f;           // this lane's share of the running sum
+    float m_run = -INFINITY;     // running max of c_log2 * s (log2 domain), lazily raised
+    float l_exp = 0.f;           // this lane's share of sum p (fp32)
+    float l_rnd = 0.f;           // this lane's share of sum bf16(p)
 
-    TileRegs<D, NW> tr;
-    load_tile<D, NW>(tr, Kh, Vh, t_lo * BC, N, tid);
-    store_tile<D, NW>(tr, lds, lds + C::K_ELEMS, tid);
-    __syncthreads();
-
-    for (int t = t_lo; t <= t_hi; ++t) {
-        const int cur = (t - t_lo) & 1;
-        __bf16* Ks = lds + cur * C::BUF_ELEMS;
-        __bf16* Vt = Ks + C::K_ELEMS;
-        if (t < t_hi) load_tile<D, NW>(tr, Kh, Vh, (t + 1) * BC, N, tid);
+    // one tile: consume buffer B (tile t), stream tile t+1 into the other buffer
+    auto step = [&](auto bufc, int t) {
+        constexpr int B = decltype(bufc)::value;
+        const char* kb = B ? lds1 : lds0;
+        const char* vb = kb + C::TILE_BYTES;
+        if (t < t_hi) load_tile(t + 1, B ? lds0 : lds1);
 
         if (t >= w_lo && t <= w_hi) {
             const int key0 = t * BC;
@@ -251,10 +249,10 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Ks + ln * C::KST + s * 16 + hl * 8);
-                const bf16x8 kb = *reinterpret_cast<const bf16x8*>(Ks + (32 + ln) * C::KST + s * 16 + hl * 8);
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + kaddr[s]);
+                const bf16x8 kc = *reinterpret_cast<const bf16x8*>(kb + kaddr[s] + 32 * CPR * 16);
                 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qreg[s], s1, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qreg[s], s1, 0, 0, 0);
             }
 
             // ---- element mask, only where the tile straddles the mask or the end
@@ -274,12 +272,13 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-            mx = wave_swap32_max(mx) * c_log2;               // full row max, scaled (c_log2 > 0)
+            mx = swap32_max(mx) * c_log2;                    // full row max, scaled (c_log2 > 0)
             const float m_new = fmaxf(m_run, mx);
             if (__any(m_new > m_run + TAU)) {
                 const float base_new = (m_new == -INFINITY) ? 0.f : m_new;
                 const float alpha = __builtin_amdgcn_exp2f(m_run - base_new);   // 0 when m_run = -inf
-                l_run *= alpha;
+                l_exp *= alpha;
+                l_rnd *= alpha;
 #pragma unroll
                 for (int j = 0; j < ND; ++j)
 #pragma unroll
@@ -288,36 +287,52 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             }
             const float base = (m_run == -INFINITY) ? 0.f : m_run;
             bf16x8 p[4];
-            float lsum = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < 16; r += 2) {
                 const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c_log2, -base));
-                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c_log2, -base));
-                lsum += e0 + e1;
-                p[r >> 3][r & 7] = (__bf16)e0;
-                p[2 + (r >> 3)][r & 7] = (__bf16)e1;
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], c_log2, -base));
+                const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c_log2, -base));
+                const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], c_log2, -base));
+                l_exp += (e0 + e1) + (e2 + e3);
+                bf16x2 pa, pb;
+                pa[0] = (__bf16)e0; pa[1] = (__bf16)e1;
+                pb[0] = (__bf16)e2; pb[1] = (__bf16)e3;
+                l_rnd = __builtin_amdgcn_fdot2_f32_bf16(pa, (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, l_rnd, false);
+                l_rnd = __builtin_amdgcn_fdot2_f32_bf16(pb, (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, l_rnd, false);
+                p[r >> 3][r & 7] = pa[0]; p[r >> 3][(r & 7) + 1] = pa[1];
+                p[2 + (r >> 3)][r & 7] = pb[0]; p[2 + (r >> 3)][(r & 7) + 1] = pb[1];
             }
-            l_run += lsum;
 
             // ---- O^T += V^T P^T : 4 slabs of 16 keys x ND blocks of 32 dims
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
                 for (int j = 0; j < ND; ++j) {
-                    const bf16x8 va = *reinterpret_cast<const bf16x8*>(Vt + (j * 32 + ln) * C::VST + ks * 16 + hl * 8);
+                    const bf16x4 lo = lds_read_tr(vb, vaddr[0][j] + ks * 16 * CPR * 16);
+                    const bf16x4 hi = lds_read_tr(vb, vaddr[1][j] + ks * 16 * CPR * 16);
+                    const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                     o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[ks], o[j], 0, 0, 0);
                 }
             }
         }
 
-        if (t < t_hi) store_tile<D, NW>(tr, lds + (cur ^ 1) * C::BUF_ELEMS, lds + (cur ^ 1) * C::BUF_ELEMS + C::K_ELEMS, tid);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+
+    load_tile(t_lo, lds0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int t = t_lo; t <= t_hi; t += 2) {
+        step(IntC<0>{}, t);
+        if (t + 1 <= t_hi) step(IntC<1>{}, t + 1);
     }
 
-    // ---- epilogue: O = acc / l (bf16, nearest even), LSE = (m + log2 l) ln 2
-    const float l_tot = wave_swap32_add(l_run);
+    // ---- epilogue: O = acc / sum bf16(p) (bf16, nearest even), LSE = (m + log2 sum p) ln 2
+    const float le = swap32_add(l_exp);
+    const float lr = swap32_add(l_rnd);
     if (my_q < N) {
-        const float inv = 1.0f / l_tot;
+        const float inv = 1.0f / lr;
         __bf16* Orow = O + head + (size_t)my_q * D;
 #pragma unroll
         for (int j = 0; j < ND; ++j) {
@@ -329,7 +344,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 *reinterpret_cast<bf16x4*>(Orow + j * 32 + 8 * g + 4 * hl) = val;
             }
         }
-        if (hl == 0) LSE[(size_t)bh * N + my_q] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+        if (hl == 0) LSE[(size_t)bh * N + my_q] = (m_run + __builtin_amdgcn_logf(le)) * 0.69314718055994531f;
     }
 }
 

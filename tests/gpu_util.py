@@ -8,6 +8,7 @@ import sys
 
 import numpy as np
 import torch
+from threadpoolctl import threadpool_limits
 
 import exact_blockwise_attention_attn_amd as attn
 from exact_blockwise_attention_attn_amd.inputs import make_qkv, row_seed, sample_rows
@@ -45,14 +46,21 @@ def oracle(qn, kn, vn, scale, mask_kind, window, rows=None):
     O = np.empty((B, H, R, qn.shape[3]))
     L = np.empty((B, H, R))
 
+    done = [0]
+    big = R * qn.shape[2] >= (1 << 26)
+
     def one(bh):
         b, h = divmod(bh, H)
         o, l = attention_forward(qn[b:b + 1, h:h + 1], kn[b:b + 1, h:h + 1], vn[b:b + 1, h:h + 1], scale,
                                  mask_kind, window, rows=rows[b, h])
         O[b, h] = o[0, 0]
         L[b, h] = l[0, 0]
+        done[0] += 1
+        if big:
+            say(f"    oracle: {done[0]}/{B * H} heads")
 
-    with cf.ThreadPoolExecutor(WORKERS) as ex:
+    # one BLAS thread per worker: the workers already cover the cores
+    with threadpool_limits(limits=1), cf.ThreadPoolExecutor(WORKERS) as ex:
         list(ex.map(one, range(B * H)))
     return O, L, rows
 
