@@ -19,10 +19,16 @@
 //
 // K/V staging.  Each K and V tile goes HBM -> LDS directly (global_load_lds_dwordx4,
 // no VGPR round trip), row-major with the 16-byte chunks of a row XOR-swizzled by
-// the row index, into one of two buffers: tile t+1 streams in while tile t is
-// consumed, one barrier per tile.  The two buffers are distinct LDS arrays and the
-// tile loop is unrolled by two, so every LDS read names its buffer statically and
-// the compiler can see it never aliases the load in flight into the other one.
+// the row index.  K and V each rotate through two buffers; one barrier per tile.
+// The four buffers are distinct LDS arrays and the tile loop is unrolled by two,
+// so every LDS read names its buffer statically and the compiler can see it never
+// aliases a load in flight into another one.
+//
+// Software pipeline.  The matrix cores compute the V product of tile t-1 while
+// the vector ALUs compute the softmax of tile t (independent streams in one basic
+// block, which the scheduler interleaves: MFMA issue between exp/fma/cvt); then
+// the scores of tile t+1.  The other wave sharing the SIMD (a second workgroup
+// per CU) fills the remaining gaps.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, 64-wide wavefront).  Each wave
 // computes the transposed score block S^T = K_tile Q_w^T (keys x queries), so a
@@ -64,34 +70,50 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-constexpr int BC = 64;              // keys per tile
 
 template <int V>
 struct IntC { static constexpr int value = V; };
-constexpr float TAU = 8.0f;         // lazy rescale threshold (log2 domain)
+constexpr float TAU = 8.0f;
 
-template <int D, int NW>
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(IntC<I>{});
+        static_for<I + 1, N>(f);
+    }
+}         // lazy rescale threshold (log2 domain)
+
+// Tile shape: a wave owns QB blocks of 32 query rows; a key tile is KB blocks of
+// 32 keys.  Each K or V operand read from LDS feeds QB matrix instructions.
+template <int D, int QB, int KB>
 struct Cfg {
+    static constexpr int NW = 4;                    // waves per workgroup, one per SIMD
+    static constexpr int RW = 32 * QB;              // query rows per wave
+    static constexpr int BC = 32 * KB;              // keys per tile
     static constexpr int NT = 64 * NW;              // threads per workgroup
-    static constexpr int BR = 32 * NW;              // query rows per workgroup
-    static constexpr int CPR = D / 8;               // 16-byte chunks per row
+    static constexpr int BR = RW * NW;              // query rows per workgroup
     static constexpr int TILE_BYTES = BC * D * 2;   // one K or V tile
-    static constexpr int BUF_BYTES = 2 * TILE_BYTES;             // K tile + V tile
-    static constexpr int LDS_BYTES = 2 * BUF_BYTES;              // both buffers
+    static constexpr int LDS_BYTES = 4 * TILE_BYTES;             // K and V, two buffers each
     static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / NW;  // 1 KB per wave instruction
+    static constexpr int RB = BC / 16;              // 16-row blocks of a tile (one 1 KB load each per chunk group)
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CDNA4 workgroup");
     static_assert(TILE_BYTES % (1024 * NW) == 0, "tile must split evenly over the waves");
     static_assert(D == 64 || D == 128, "head dim");
 };
 
-// XOR applied to the chunk index of a row.  It makes both LDS read patterns
-// conflict-free on 64 banks: 16 consecutive rows at one chunk (K operand, 16-byte
-// reads) and 4 consecutive rows x 4 consecutive chunks (V operand, transposing
-// 8-byte reads).
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-    if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
-    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+// LDS layout of a K or V tile (BC rows x D/8 16-byte chunks).  Chunks are grouped
+// four at a time (64 bytes of a row); group J holds the chunks 4J..4J+3 of every
+// row contiguously, row after row, and inside a row the four chunks are XOR-ed
+// with (row / 4) mod 4:
+//     slot(row, c) = (c / 4) * 4 BC + 4 row + ((c mod 4) ^ ((row / 4) mod 4))
+// One 1 KB load instruction fills 16 rows of one group (64 contiguous bytes of
+// each row: coalesced).  Both LDS read patterns are conflict-free on 64 banks:
+// 16 consecutive rows at one chunk (K operand, 16-byte reads) and 4 consecutive
+// rows x 4 chunks of a group (V operand, transposing 8-byte reads), and every read
+// address is a per-lane base plus compile-time offsets.
+template <int BC>
+__device__ __forceinline__ int slot_of(int row, int c) {
+    return (c >> 2) * (4 * BC) + 4 * row + ((c & 3) ^ ((row >> 2) & 3));
 }
 
 __device__ __forceinline__ float swap32_max(float x) {
@@ -112,8 +134,8 @@ __device__ __forceinline__ bool key_allowed(int qi, int kj, int N, int window) {
     return true;
 }
 
-// Inclusive key-tile range holding an allowed key for some row of [r0, r1].
-template <int MASK>
+// Inclusive key-tile range (tiles of BC keys) holding an allowed key for some row of [r0, r1].
+template <int MASK, int BC>
 __device__ __forceinline__ void tile_range(int r0, int r1, int N, int window, int& lo, int& hi) {
     const int last = (N - 1) / BC;
     if (MASK == ATTN_MASK_CAUSAL) {
@@ -133,17 +155,43 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const char* lds_base, int byte_off
     return __builtin_bit_cast(bf16x4, r);
 }
 
-template <int D, int NW, int MASK>
-__global__ __launch_bounds__(64 * NW, 2)
+// Score MFMAs with the read-only Q operands pinned to the AGPR file
+// (v_mfma_f32_32x32x16_bf16, acc += A B, accumulator in VGPRs).  At 64 query
+// rows per wave, O (VGPRs, compiler-issued MFMAs), S, P and the temporaries fill
+// the VGPR file; Q alone goes to the AGPRs.  The compiler cannot see into these
+// asm statements, so the hazards it would pad are handled here: the chain
+// accumulates back to back into the same registers (interlocked by hardware);
+// settle_v() puts >= 18 wait states before any vector-ALU read of S, tied to S
+// as an operand so nothing is scheduled across it; the A operand comes straight
+// from an LDS load and Q is pinned (and padded) once at kernel start.
+__device__ __forceinline__ void mfma_s_first(f32x16& acc, const bf16x8& a, const bf16x8& q) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void mfma_s(f32x16& acc, const bf16x8& a, const bf16x8& q) {
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(q));
+}
+__device__ __forceinline__ void settle_qa(bf16x8& x) {     // pin an operand into AGPRs, padded
+    asm volatile("s_nop 4" : "+a"(x));
+}
+__device__ __forceinline__ void settle_v(f32x16& x) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
+}
+
+template <int D, int QB, int KB, int MASK>
+__global__ __launch_bounds__(256, 1)
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
                 int BH, int N, int nqt, float c_log2, int negate_q, int window) {
-    using C = Cfg<D, NW>;
+    using C = Cfg<D, QB, KB>;
+    constexpr int BC = C::BC;
     constexpr int NS = D / 16;       // 16-dim slabs of the contraction over d
     constexpr int ND = D / 32;       // 32-row blocks of O^T
-    constexpr int CPR = C::CPR;
-    __shared__ __attribute__((aligned(1024))) char lds0[C::BUF_BYTES];
-    __shared__ __attribute__((aligned(1024))) char lds1[C::BUF_BYTES];
+    constexpr int NKS = BC / 16;     // 16-key slabs of the V product
+    // K and V tiles rotate through two buffers each; four distinct arrays
+    __shared__ __attribute__((aligned(1024))) char kbuf0[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char kbuf1[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char vbuf0[C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[C::TILE_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -165,206 +213,384 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* Kh = K + head;
     const __bf16* Vh = V + head;
 
-    const int qw0 = q0 + wave * 32;              // first row of this wave
-    const int my_q = qw0 + ln;                   // the query this lane's column holds
-    const int qrow = min(my_q, N - 1);
-
-    // Q operand (B of S^T = K Q^T): lane holds Q[my_q][16 s + 8 hl .. +8].
-    bf16x8 qreg[NS];
+    const int qw0 = q0 + wave * C::RW;           // first row of this wave
+    int my_q[QB];                                // the query of this lane's column in each 32-row block
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        u32x4 raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)qrow * D + s * 16 + hl * 8);
-        if (negate_q) raw ^= 0x80008000u;        // exact sign flip: scale < 0 runs as -q with |scale|
-        qreg[s] = __builtin_bit_cast(bf16x8, raw);
-    }
+    for (int b = 0; b < QB; ++b) my_q[b] = qw0 + 32 * b + ln;
 
-    // ---- per-lane LDS addresses (byte offsets within a K or V tile)
-    // loader: wave instruction i fills 1 KB block b = wave * LPW + i; lane -> slot
-    int ld_row[C::LOADS_PER_WAVE], ld_col[C::LOADS_PER_WAVE];
+    // Q operands (B of S^T = K Q^T): lane holds Q[my_q[b]][16 s + 8 hl .. +8].
+    bf16x8 qreg[QB][NS];
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            u32x4 raw = *reinterpret_cast<const u32x4*>(Qh + (size_t)min(my_q[b], N - 1) * D + s * 16 + hl * 8);
+            if (negate_q) raw ^= 0x80008000u;    // exact sign flip: scale < 0 runs as -q with |scale|
+            qreg[b][s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    // the operands sit in AGPRs from here on, written (and padded) well before any MFMA reads them
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) settle_qa(qreg[b][s]);
+
+    // ---- per-lane LDS and load addresses (byte offsets within a tile)
+    // loader: wave instruction i fills 1 KB block b = wave * LPW + i, i.e. rows
+    // 16 (b % RB) .. +15 of chunk group b / RB; lane -> (row, chunk)
+    uint32_t ld_off[C::LOADS_PER_WAVE];          // byte offset of the lane's 16 bytes in the HBM tile
 #pragma unroll
     for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
-        const int slot = (wave * C::LOADS_PER_WAVE + i) * 64 + lane;
-        const int row = slot / CPR;
-        ld_row[i] = row;
-        ld_col[i] = ((slot % CPR) ^ swz<D>(row)) * 8;
+        const int b = wave * C::LOADS_PER_WAVE + i;
+        const int row = 16 * (b % C::RB) + (lane >> 2);
+        const int c = 4 * (b / C::RB) + ((lane & 3) ^ ((row >> 2) & 3));
+        ld_off[i] = (uint32_t)(row * D + c * 8) * 2u;
     }
-    // K operand: row ln (and 32 + ln, same swizzle), chunk 2 s + hl
-    int kaddr[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) kaddr[s] = (ln * CPR + ((2 * s + hl) ^ swz<D>(ln))) * 16;
-    // V operand: transposing reads; read r of d-block j, supplier lane (g, s16)
-    int vaddr[2][ND];
+    // K operand: row 32 kb + ln, chunk 2 s + hl = group s / 2, in-group 2 (s % 2) + hl
+    const int sw = (ln >> 2) & 3;
+    const int kaddr_e = (4 * ln + (hl ^ sw)) * 16;          // s even
+    const int kaddr_o = (4 * ln + ((2 + hl) ^ sw)) * 16;    // s odd
+    // V operand (transposing reads), read r: supplier lane (g, s16) names key row
+    // 8 r + 4 hl + s16 / 4 of the slab and 8 bytes of chunk 4 j + 2 (g % 2) + (s16 % 4) / 2
+    int vaddr[2];
     {
         const int g = lane >> 4, s16 = lane & 15;
+        const int k = 2 * (g & 1) + ((s16 & 3) >> 1);
 #pragma unroll
         for (int r = 0; r < 2; ++r)
-#pragma unroll
-            for (int j = 0; j < ND; ++j) {
-                const int rr = 8 * r + 4 * hl + (s16 >> 2);                 // key within a 16-key slab
-                const int chunk = 4 * j + 2 * (g & 1) + ((s16 & 3) >> 1);
-                vaddr[r][j] = (rr * CPR + (chunk ^ swz<D>(rr))) * 16 + (s16 & 1) * 8;
-            }
+            vaddr[r] = ((8 * r + 4 * hl + (s16 >> 2)) * 4 + (k ^ (2 * r + hl))) * 16 + (s16 & 1) * 8;
     }
 
     int t_lo, t_hi;
-    tile_range<MASK>(q0, min(q0 + C::BR, N) - 1, N, window, t_lo, t_hi);
-    int w_lo = 1, w_hi = 0;                      // this wave's own tile range (empty if no rows)
-    if (qw0 < N) tile_range<MASK>(qw0, min(qw0 + 31, N - 1), N, window, w_lo, w_hi);
+    tile_range<MASK, BC>(q0, min(q0 + C::BR, N) - 1, N, window, t_lo, t_hi);
+    const int n_tiles = t_hi - t_lo + 1;
 
-    // issue the direct HBM -> LDS loads of key tile t into buffer `kb`
-    auto load_tile = [&](int t, char* kb) {
+    // direct HBM -> LDS load of tile t of one tensor into `dst` (this wave's share)
+    auto dma = [&](const __bf16* src, int t, char* dst) __attribute__((always_inline)) {
         const int key0 = t * BC;
-        char* vb = kb + C::TILE_BYTES;
+        const char* base = reinterpret_cast<const char*>(src + (size_t)key0 * D);
+        if (key0 + BC <= N) {
 #pragma unroll
-        for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
-            const int row = min(key0 + ld_row[i], N - 1);       // rows past the end: any valid row, masked later
-            const size_t off = (size_t)row * D + ld_col[i];
-            const int blk = (wave * C::LOADS_PER_WAVE + i) * 1024;
-            __builtin_amdgcn_global_load_lds((const void*)(Kh + off), (lds_void*)(kb + blk), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(Vh + off), (lds_void*)(vb + blk), 16, 0, 0);
+            for (int i = 0; i < C::LOADS_PER_WAVE; ++i)
+                __builtin_amdgcn_global_load_lds((const void*)(base + ld_off[i]),
+                                                 (lds_void*)(dst + (wave * C::LOADS_PER_WAVE + i) * 1024), 16, 0, 0);
+        } else {
+            // last tile: rows past the end load row N - 1 (any valid row; masked later)
+            const int rows_left = N - 1 - key0;
+#pragma unroll
+            for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
+                const int row = (int)(ld_off[i] / (2 * D));
+                const uint32_t off = ld_off[i] - (uint32_t)(row - min(row, rows_left)) * (2 * D);
+                __builtin_amdgcn_global_load_lds((const void*)(base + off),
+                                                 (lds_void*)(dst + (wave * C::LOADS_PER_WAVE + i) * 1024), 16, 0, 0);
+            }
         }
     };
 
-    f32x16 o[ND];
+    f32x16 o[QB][ND];
 #pragma unroll
-    for (int j = 0; j < ND; ++j)
+    for (int b = 0; b < QB; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
-    float m_run = -INFINITY;     // running max of c_log2 * s (log2 domain), lazily raised
-    float l_exp = 0.f;           // this lane's share of sum p (fp32)
-    float l_rnd = 0.f;           // this lane's share of sum bf16(p)
+        for (int j = 0; j < ND; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[b][j][r] = 0.f;
+    float m_run[QB], l_exp[QB], l_rnd[QB];     // running max (log2 domain, lazily raised), sum p, sum bf16(p)
+#pragma unroll
+    for (int b = 0; b < QB; ++b) { m_run[b] = -INFINITY; l_exp[b] = 0.f; l_rnd[b] = 0.f; }
+    f32x16 sc[2][QB][KB];                      // S^T of two tiles (alternating): [query block][32-key block]
+    bf16x8 pr[2][QB][NKS];                     // P^T of two tiles (alternating), [query block][16-key slab]
 
-    // one tile: consume buffer B (tile t), stream tile t+1 into the other buffer
-    auto step = [&](auto bufc, int t) {
-        constexpr int B = decltype(bufc)::value;
-        const char* kb = B ? lds1 : lds0;
-        const char* vb = kb + C::TILE_BYTES;
-        if (t < t_hi) load_tile(t + 1, B ? lds0 : lds1);
-
-        if (t >= w_lo && t <= w_hi) {
-            const int key0 = t * BC;
-            // ---- S^T = K_tile Q^T : two 32-key blocks x 32 queries
-            f32x16 s0, s1;
+    // S^T = K_tile Q^T into sc[X]; each K operand read feeds QB matrix instructions
+    auto scores = [&](auto xc, const char* kb) __attribute__((always_inline)) {
+        constexpr int X = decltype(xc)::value;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+        for (int s = 0; s < NS; ++s) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kb + kaddr[s]);
-                const bf16x8 kc = *reinterpret_cast<const bf16x8*>(kb + kaddr[s] + 32 * CPR * 16);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[s], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc, qreg[s], s1, 0, 0, 0);
-            }
-
-            // ---- element mask, only where the tile straddles the mask or the end
-            bool need_mask = key0 + BC > N;
-            if (MASK == ATTN_MASK_CAUSAL) need_mask |= key0 + BC - 1 > qw0;
-            if (MASK == ATTN_MASK_WINDOW) need_mask |= (key0 < qw0 + 31 - window) || (key0 + BC - 1 > qw0 + window);
-            if (need_mask) {
+            for (int k = 0; k < KB; ++k) {
+                const char* kp = kb + (s >> 1) * (4 * BC * 16) + k * (32 * 4 * 16) + ((s & 1) ? kaddr_o : kaddr_e);
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kk = key0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    if (!key_allowed<MASK>(my_q, kk, N, window)) s0[r] = -INFINITY;
-                    if (!key_allowed<MASK>(my_q, kk + 32, N, window)) s1[r] = -INFINITY;
-                }
-            }
-
-            // ---- online softmax (log2 domain, lazy rescale)
-            float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-            mx = swap32_max(mx) * c_log2;                    // full row max, scaled (c_log2 > 0)
-            const float m_new = fmaxf(m_run, mx);
-            if (__any(m_new > m_run + TAU)) {
-                const float base_new = (m_new == -INFINITY) ? 0.f : m_new;
-                const float alpha = __builtin_amdgcn_exp2f(m_run - base_new);   // 0 when m_run = -inf
-                l_exp *= alpha;
-                l_rnd *= alpha;
-#pragma unroll
-                for (int j = 0; j < ND; ++j)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
-                m_run = m_new;
-            }
-            const float base = (m_run == -INFINITY) ? 0.f : m_run;
-            bf16x8 p[4];
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r], c_log2, -base));
-                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[r + 1], c_log2, -base));
-                const float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r], c_log2, -base));
-                const float e3 = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r + 1], c_log2, -base));
-                l_exp += (e0 + e1) + (e2 + e3);
-                bf16x2 pa, pb;
-                pa[0] = (__bf16)e0; pa[1] = (__bf16)e1;
-                pb[0] = (__bf16)e2; pb[1] = (__bf16)e3;
-                l_rnd = __builtin_amdgcn_fdot2_f32_bf16(pa, (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, l_rnd, false);
-                l_rnd = __builtin_amdgcn_fdot2_f32_bf16(pb, (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, l_rnd, false);
-                p[r >> 3][r & 7] = pa[0]; p[r >> 3][(r & 7) + 1] = pa[1];
-                p[2 + (r >> 3)][r & 7] = pb[0]; p[2 + (r >> 3)][(r & 7) + 1] = pb[1];
-            }
-
-            // ---- O^T += V^T P^T : 4 slabs of 16 keys x ND blocks of 32 dims
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-                for (int j = 0; j < ND; ++j) {
-                    const bf16x4 lo = lds_read_tr(vb, vaddr[0][j] + ks * 16 * CPR * 16);
-                    const bf16x4 hi = lds_read_tr(vb, vaddr[1][j] + ks * 16 * CPR * 16);
-                    const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                    o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[ks], o[j], 0, 0, 0);
+                for (int b = 0; b < QB; ++b) {
+                    if (s == 0) mfma_s_first(sc[X][b][k], ka, qreg[b][s]);
+                    else mfma_s(sc[X][b][k], ka, qreg[b][s]);
                 }
             }
         }
+    };
+    // >= 18 wait states before the vector ALUs read sc[X]
+    auto settle_scores = [&](auto xc) __attribute__((always_inline)) {
+        constexpr int X = decltype(xc)::value;
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int k = 0; k < KB; ++k) settle_v(sc[X][b][k]);
+    };
 
+    // allowed keys of each row form one interval [key_lo, key_hi] (the mask and the
+    // sequence end together); element masking is one unsigned range test per score
+    int key_lo[QB], key_span[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+        const int qi = min(my_q[b], N - 1);
+        int lo = 0, hi = N - 1;
+        if (MASK == ATTN_MASK_CAUSAL) hi = qi;
+        if (MASK == ATTN_MASK_WINDOW) { lo = max(0, qi - window); hi = min(N - 1, qi + window); }
+        key_lo[b] = lo;
+        key_span[b] = hi - lo;
+    }
+
+    // element mask of tile t, only where the tile straddles the mask or the end (a
+    // tile with no allowed key for a row leaves it all -inf, so its p = 0)
+    auto mask_tile = [&](auto xc, int t) __attribute__((always_inline)) {
+        constexpr int X = decltype(xc)::value;
+        const int key0 = t * BC;
+        bool need = key0 + BC > N;
+        if (MASK == ATTN_MASK_CAUSAL) need |= key0 + BC - 1 > qw0;
+        if (MASK == ATTN_MASK_WINDOW) need |= (key0 < qw0 + C::RW - 1 - window) || (key0 + BC - 1 > qw0 + window);
+        if (need) {
+            asm volatile("" ::: "memory");   // a side effect: keeps this a branch, not selects on every tile
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                const int rel = key0 + 4 * hl - key_lo[b];       // key of element r is rel + offset(r) past key_lo
+#pragma unroll
+                for (int k = 0; k < KB; ++k)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = 32 * k + 8 * (r >> 2) + (r & 3);
+                        if ((unsigned)(rel + off) > (unsigned)key_span[b]) sc[X][b][k][r] = -INFINITY;
+                    }
+            }
+        }
+    };
+
+    // O^T += V^T P^T with pr[X]; each V operand read feeds QB matrix instructions
+    auto pv = [&](auto xc, const char* vb) __attribute__((always_inline)) {
+        constexpr int X = decltype(xc)::value;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+            for (int j = 0; j < ND; ++j) {
+                const bf16x4 lo = lds_read_tr(vb, j * (4 * BC * 16) + ks * (16 * 4 * 16) + vaddr[0]);
+                const bf16x4 hi = lds_read_tr(vb, j * (4 * BC * 16) + ks * (16 * 4 * 16) + vaddr[1]);
+                const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                for (int b = 0; b < QB; ++b)
+                    o[b][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pr[X][b][ks], o[b][j], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- one key tile as a fixed instruction schedule
+    // The work of a tile is three independent streams:
+    //     matrix cores : S(t+1) = K(t+1) Q^T  (NSM instructions), then O += V(t-1)^T P(t-1)  (NPM)
+    //     vector ALUs  : softmax of S(t) -> P(t)  (NTASK tasks: row maxima, then one task per score)
+    //     LDS reads    : the K and V operands, a few matrix instructions ahead of their use
+    // They are laid out by hand, one matrix instruction per slot with a share of the
+    // softmax behind it, and the compiler's scheduler is fenced between slots, so the
+    // vector work runs while the matrix cores are busy instead of after them.
+    constexpr int NSM = NS * QB;                 // score instructions per tile
+    constexpr int NPC = NKS * ND;                // V operands per tile
+    constexpr int NPM = NPC * QB;                // V-product instructions per tile
+    constexpr int NSLOT = NSM + NPM;
+    constexpr int NEL = 16 * QB;                 // scores per lane per tile (KB = 1)
+    constexpr int NTASK = 2 * QB + NEL + 1;      // maxima (2 per block), scores, sum update
+    constexpr int KPRE = 3;                      // K operands read before the first slot
+    constexpr int VLEAD = 4;                     // slots between a V read and its first use
+    static_assert(KB == 1, "the schedule assumes 32-key tiles");
+
+    auto read_k = [&](const char* kb, int s) __attribute__((always_inline)) -> bf16x8 {
+        return *reinterpret_cast<const bf16x8*>(kb + (s >> 1) * (4 * BC * 16) + ((s & 1) ? kaddr_o : kaddr_e));
+    };
+    auto read_v = [&](const char* vb, int c) __attribute__((always_inline)) -> bf16x8 {
+        const int ks = c / ND, j = c % ND;
+        const bf16x4 lo = lds_read_tr(vb, j * (4 * BC * 16) + ks * (16 * 4 * 16) + vaddr[0]);
+        const bf16x4 hi = lds_read_tr(vb, j * (4 * BC * 16) + ks * (16 * 4 * 16) + vaddr[1]);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+
+    // softmax task k of S(t) in sc[X]
+    auto task = [&](auto xc, auto kc, float* mx, float* base, float* alpha, float* se, float* sr,
+                    float (*ev)[16], bool& raise_any) __attribute__((always_inline)) {
+        constexpr int X = decltype(xc)::value;
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k < 2 * QB && k % 2 == 0) {            // lane maximum of block b (v_max3 chain)
+            constexpr int b = k / 2;
+            float m = fmaxf(fmaxf(sc[X][b][0][0], sc[X][b][0][1]), sc[X][b][0][2]);
+#pragma unroll
+            for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, sc[X][b][0][r]), sc[X][b][0][r + 1]);
+            mx[b] = fmaxf(m, sc[X][b][0][15]);
+        } else if constexpr (k < 2 * QB) {                   // row maximum, lazy raise (wave vote)
+            constexpr int b = k / 2;
+            const float mrow = swap32_max(mx[b]) * c_log2;
+            const float m_new = fmaxf(m_run[b], mrow);
+            const bool raise = __any(m_new > m_run[b] + TAU);
+            raise_any |= raise;
+            const float m_use = raise ? m_new : m_run[b];
+            base[b] = (m_use == -INFINITY) ? 0.f : m_use;
+            alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - base[b]);   // 1 unless raised; 0 when m_run = -inf
+            m_run[b] = m_use;
+            se[b] = 0.f;
+            sr[b] = 0.f;
+        } else if constexpr (k < 2 * QB + NEL) {             // one probability
+            constexpr int h = k - 2 * QB, b = h / 16, r = h % 16;
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[X][b][0][r], c_log2, -base[b]));
+            se[b] += e;
+            ev[b][r] = e;
+            if constexpr (r & 1) {
+                bf16x2 pa;
+                pa[0] = (__bf16)ev[b][r - 1];
+                pa[1] = (__bf16)e;
+                sr[b] = __builtin_amdgcn_fdot2_f32_bf16(pa, (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, sr[b], false);
+                // keys 8 (r/4) + 4 hl + r % 4: slab r / 8, position r % 8
+                pr[X][b][r >> 3][(r & 7) - 1] = pa[0];
+                pr[X][b][r >> 3][r & 7] = pa[1];
+            }
+        } else {                                             // running sums
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                l_exp[b] = __builtin_fmaf(alpha[b], l_exp[b], se[b]);
+                l_rnd[b] = __builtin_fmaf(alpha[b], l_rnd[b], sr[b]);
+            }
+        }
+    };
+
+    // rare (the maximum grows by > TAU); kept as a real branch (the empty asm is a
+    // side effect the compiler may not speculate), so O is not touched on other tiles
+    auto rescale_o = [&](const float* alpha) __attribute__((always_inline)) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int b = 0; b < QB; ++b)
+#pragma unroll
+            for (int j = 0; j < ND; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[b][j][r] *= alpha[b];
+    };
+
+    // Tiles u = 0 .. n_tiles - 1 (t = t_lo + u).  K(t) lives in kbuf[u % 2], V(t) in
+    // vbuf[u % 2], S(t) in sc[u % 2], P(t) in pr[u % 2].  Tile u streams K(t+2) and
+    // V(t) into LDS, masks S(t) where the tile straddles the mask, then runs the
+    // fixed schedule and one barrier.  Every wave runs every tile of the workgroup's
+    // range (a tile outside its rows' mask comes out with p = 0); the last tile's
+    // score stream reads a stale buffer and its result is never used.  P starts at
+    // zero and vbuf1 is zero-filled, so the first V product adds 0.
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int k = 0; k < NKS; ++k) { pr[0][b][k] = (bf16x8){}; pr[1][b][k] = (bf16x8){}; }
+    for (int i = tid * 16; i < C::TILE_BYTES; i += C::NT * 16)
+        *reinterpret_cast<u32x4*>(vbuf1 + i) = (u32x4){0u, 0u, 0u, 0u};
+    dma(Kh, t_lo, kbuf0);
+    if (n_tiles > 1) dma(Kh, t_lo + 1, kbuf1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    scores(IntC<0>{}, kbuf0);
+    settle_scores(IntC<0>{});
+    __syncthreads();     // every wave is done with K(t_lo) before tile 0 refills its buffer
+
+    auto iter = [&](auto parity, int u) __attribute__((always_inline)) {
+        constexpr int B = decltype(parity)::value;        // u % 2
+        constexpr int X = 1 - B;
+        const int t = t_lo + u;
+        char* k_own = B ? kbuf1 : kbuf0;                  // held K(t) (consumed); receives K(t+2)
+        const char* k_next = B ? kbuf0 : kbuf1;           // K(t+1)
+        char* v_own = B ? vbuf1 : vbuf0;                  // held V(t-2) (consumed); receives V(t)
+        const char* v_prev = B ? vbuf0 : vbuf1;           // V(t-1)
+        if (u + 2 < n_tiles) dma(Kh, t + 2, k_own);
+        dma(Vh, t, v_own);
+        mask_tile(IntC<B>{}, t);
+
+        float mx[QB], base[QB], alpha[QB], se[QB], sr[QB];
+        float ev[QB][16];
+        bool raise_any = false;
+        bf16x8 ka[NS], va[NPC];
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, KPRE>([&](auto sc_) { ka[decltype(sc_)::value] = read_k(k_next, decltype(sc_)::value); });
+        task(IntC<B>{}, IntC<0>{}, mx, base, alpha, se, sr, ev, raise_any);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, NSLOT>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            // matrix instruction of slot i
+            if constexpr (i < NSM) {
+                constexpr int s = i / QB, b = i % QB;
+                if constexpr (s == 0) mfma_s_first(sc[X][b][0], ka[s], qreg[b][s]);
+                else mfma_s(sc[X][b][0], ka[s], qreg[b][s]);
+            } else {
+                constexpr int c = (i - NSM) / QB, b = (i - NSM) % QB;
+                o[b][c % ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c], pr[X][b][c / ND], o[b][c % ND], 0, 0, 0);
+            }
+            // LDS reads for later slots
+            if constexpr (i < NSM && i % QB == 0 && i / QB + KPRE < NS) ka[i / QB + KPRE] = read_k(k_next, i / QB + KPRE);
+            static_for<0, NPC>([&](auto cc) {
+                constexpr int c = decltype(cc)::value;
+                if constexpr (NSM + QB * c - VLEAD == i || (i == 0 && NSM + QB * c - VLEAD < 0)) va[c] = read_v(v_prev, c);
+            });
+            // softmax tasks of slot i: task k (>= 1) runs in slot (k - 1) NSLOT / (NTASK - 1)
+            static_for<1, NTASK>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if constexpr ((k - 1) * NSLOT / (NTASK - 1) == i) task(IntC<B>{}, kc, mx, base, alpha, se, sr, ev, raise_any);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        // the softmax results are consumed here (an empty asm), so they cannot sink below the branch
+#pragma unroll
+        for (int b = 0; b < QB; ++b) {
+            asm volatile("" ::"v"(l_exp[b]), "v"(l_rnd[b]));
+#pragma unroll
+            for (int k = 0; k < NKS; ++k) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pr[B][b][k])));
+        }
+        if (raise_any) rescale_o(alpha);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
-
-    load_tile(t_lo, lds0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int t = t_lo; t <= t_hi; t += 2) {
-        step(IntC<0>{}, t);
-        if (t + 1 <= t_hi) step(IntC<1>{}, t + 1);
+    int u = 0;
+    for (; u + 1 < n_tiles; u += 2) {
+        iter(IntC<0>{}, u);
+        iter(IntC<1>{}, u + 1);
     }
+    if (u < n_tiles) iter(IntC<0>{}, u++);
+    // closing step: the V product of the last tile (V(n_tiles - 1) in vbuf[(n_tiles - 1) % 2])
+    if (u & 1) pv(IntC<0>{}, vbuf0); else pv(IntC<1>{}, vbuf1);
 
     // ---- epilogue: O = acc / sum bf16(p) (bf16, nearest even), LSE = (m + log2 sum p) ln 2
-    const float le = swap32_add(l_exp);
-    const float lr = swap32_add(l_rnd);
-    if (my_q < N) {
-        const float inv = 1.0f / lr;
-        __bf16* Orow = O + head + (size_t)my_q * D;
 #pragma unroll
-        for (int j = 0; j < ND; ++j) {
+    for (int b = 0; b < QB; ++b) {
+        const float le = swap32_add(l_exp[b]);
+        const float lr = swap32_add(l_rnd[b]);
+        if (my_q[b] < N) {
+            const float inv = 1.0f / lr;
+            __bf16* Orow = O + head + (size_t)my_q[b] * D;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                bf16x4 val;
+            for (int j = 0; j < ND; ++j) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[j][4 * g + e] * inv);
-                *reinterpret_cast<bf16x4*>(Orow + j * 32 + 8 * g + 4 * hl) = val;
+                for (int g = 0; g < 4; ++g) {
+                    bf16x4 val;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[b][j][4 * g + e] * inv);
+                    *reinterpret_cast<bf16x4*>(Orow + j * 32 + 8 * g + 4 * hl) = val;
+                }
             }
+            if (hl == 0)
+                LSE[(size_t)bh * N + my_q[b]] = (m_run[b] + __builtin_amdgcn_logf(le)) * 0.69314718055994531f;
         }
-        if (hl == 0) LSE[(size_t)bh * N + my_q] = (m_run + __builtin_amdgcn_logf(le)) * 0.69314718055994531f;
     }
 }
 
-template <int D, int NW, int MASK>
+template <int D, int QB, int KB, int MASK>
 static int launch(const AttnLaunch& a) {
-    using C = Cfg<D, NW>;
+    using C = Cfg<D, QB, KB>;
     const int nqt = (a.N + C::BR - 1) / C::BR;
     const long long grid = (long long)nqt * a.B * a.H;
-    hipLaunchKernelGGL((fwd_kernel<D, NW, MASK>), dim3((unsigned)grid), dim3(C::NT), 0, (hipStream_t)a.stream,
+    hipLaunchKernelGGL((fwd_kernel<D, QB, KB, MASK>), dim3((unsigned)grid), dim3(C::NT), 0, (hipStream_t)a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.out, a.lse,
                        a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window);
     return 0;
 }
 
-template <int D, int NW>
+template <int D, int QB, int KB>
 static int by_mask(const AttnLaunch& a) {
     switch (a.mask_kind) {
-        case ATTN_MASK_CAUSAL: return launch<D, NW, ATTN_MASK_CAUSAL>(a);
-        case ATTN_MASK_WINDOW: return launch<D, NW, ATTN_MASK_WINDOW>(a);
-        default: return launch<D, NW, ATTN_MASK_NONE>(a);
+        case ATTN_MASK_CAUSAL: return launch<D, QB, KB, ATTN_MASK_CAUSAL>(a);
+        case ATTN_MASK_WINDOW: return launch<D, QB, KB, ATTN_MASK_WINDOW>(a);
+        default: return launch<D, QB, KB, ATTN_MASK_NONE>(a);
     }
 }
 
@@ -372,6 +598,6 @@ static int by_mask(const AttnLaunch& a) {
 
 int attn_launch_bf16(const AttnLaunch& a) {
     using namespace attn_bf16;
-    if (a.d == 128) return by_mask<128, 4>(a);
-    return by_mask<64, 4>(a);
+    if (a.d == 128) return by_mask<128, 2, 1>(a);
+    return by_mask<64, 2, 1>(a);
 }
