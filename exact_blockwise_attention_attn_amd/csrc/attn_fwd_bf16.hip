@@ -392,7 +392,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     constexpr int NPM = NPC * QB;                // V-product instructions per tile
     constexpr int NSLOT = NSM + NPM;
     constexpr int NEL = 16 * QB;                 // scores per lane per tile (KB = 1)
-    constexpr int NTASK = 2 * QB + NEL + 1;      // maxima (2 per block), scores, sum update
+    constexpr int NTASK = QB + 1 + NEL + 1;      // lane maxima, vote, scores, sum update
     constexpr int KPRE = 3;                      // K operands read before the first slot
     constexpr int VLEAD = 4;                     // slots between a V read and its first use
     static_assert(KB == 1, "the schedule assumes 32-key tiles");
@@ -407,39 +407,60 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
 
+    // reference state per query block: m_run (log2 domain, -inf before any allowed
+    // key), the exponent offset base_run (m_run, or 0 while m_run = -inf) and
+    // thr_raw = (m_run + TAU) / c, the raw score above which the reference is raised
+    float base_run[QB], thr_raw[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) { base_run[b] = 0.f; thr_raw[b] = -INFINITY; }
+    const float inv_c = 1.0f / c_log2;
+
     // softmax task k of S(t) in sc[X]
-    auto task = [&](auto xc, auto kc, float* mx, float* base, float* alpha, float* se, float* sr,
+    auto task = [&](auto xc, auto kc, float* mx, float* alpha, float* se, float* sr,
                     float (*ev)[16], bool& raise_any) __attribute__((always_inline)) {
         constexpr int X = decltype(xc)::value;
         constexpr int k = decltype(kc)::value;
-        if constexpr (k < 2 * QB && k % 2 == 0) {            // lane maximum of block b (v_max3 chain)
-            constexpr int b = k / 2;
+        if constexpr (k < QB) {                              // lane maximum of block k (v_max3 chain)
+            constexpr int b = k;
             float m = fmaxf(fmaxf(sc[X][b][0][0], sc[X][b][0][1]), sc[X][b][0][2]);
 #pragma unroll
             for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, sc[X][b][0][r]), sc[X][b][0][r + 1]);
             mx[b] = fmaxf(m, sc[X][b][0][15]);
-        } else if constexpr (k < 2 * QB) {                   // row maximum, lazy raise (wave vote)
-            constexpr int b = k / 2;
-            const float mrow = swap32_max(mx[b]) * c_log2;
-            const float m_new = fmaxf(m_run[b], mrow);
-            const bool raise = __any(m_new > m_run[b] + TAU);
-            raise_any |= raise;
-            const float m_use = raise ? m_new : m_run[b];
-            base[b] = (m_use == -INFINITY) ? 0.f : m_use;
-            alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - base[b]);   // 1 unless raised; 0 when m_run = -inf
-            m_run[b] = m_use;
-            se[b] = 0.f;
-            sr[b] = 0.f;
-        } else if constexpr (k < 2 * QB + NEL) {             // one probability
-            constexpr int h = k - 2 * QB, b = h / 16, r = h % 16;
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[X][b][0][r], c_log2, -base[b]));
-            se[b] += e;
+        } else if constexpr (k == QB) {                      // wave vote: does any row pass its threshold?
+            bool over = false;
+#pragma unroll
+            for (int b = 0; b < QB; ++b) { over |= mx[b] > thr_raw[b]; alpha[b] = 1.f; }
+            raise_any = __any(over);
+            if (raise_any) {
+                // rare: every row of the wave takes its exact running maximum as reference
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int b = 0; b < QB; ++b) {
+                    const float m_new = fmaxf(m_run[b], swap32_max(mx[b]) * c_log2);
+                    const float base = (m_new == -INFINITY) ? 0.f : m_new;
+                    alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - base);   // 0 while m_run = -inf
+                    m_run[b] = m_new;
+                    base_run[b] = base;
+                    thr_raw[b] = (m_new + TAU) * inv_c;
+                }
+            }
+        } else if constexpr (k < QB + 1 + NEL) {             // one probability
+            constexpr int h = k - QB - 1, b = h / 16, r = h % 16;
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[X][b][0][r], c_log2, -base_run[b]));
+            se[b] = (r == 0) ? e : se[b] + e;
             ev[b][r] = e;
             if constexpr (r & 1) {
                 bf16x2 pa;
                 pa[0] = (__bf16)ev[b][r - 1];
                 pa[1] = (__bf16)e;
-                sr[b] = __builtin_amdgcn_fdot2_f32_bf16(pa, (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, sr[b], false);
+#ifdef RSUM_DOT2
+                sr[b] = __builtin_amdgcn_fdot2_f32_bf16(pa, (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, r == 1 ? 0.f : sr[b], false);
+#else
+                // sum of the rounded pair: the two bf16 halves read back as fp32
+                const uint32_t pb = __builtin_bit_cast(uint32_t, pa);
+                const float lo = __uint_as_float(pb << 16), hi = __uint_as_float(pb & 0xffff0000u);
+                sr[b] = (r == 1) ? lo + hi : sr[b] + lo + hi;
+#endif
                 // keys 8 (r/4) + 4 hl + r % 4: slab r / 8, position r % 8
                 pr[X][b][r >> 3][(r & 7) - 1] = pa[0];
                 pr[X][b][r >> 3][r & 7] = pa[1];
@@ -498,13 +519,13 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         dma(Vh, t, v_own);
         mask_tile(IntC<B>{}, t);
 
-        float mx[QB], base[QB], alpha[QB], se[QB], sr[QB];
+        float mx[QB], alpha[QB], se[QB], sr[QB];
         float ev[QB][16];
         bool raise_any = false;
         bf16x8 ka[NS], va[NPC];
         __builtin_amdgcn_sched_barrier(0);
         static_for<0, KPRE>([&](auto sc_) { ka[decltype(sc_)::value] = read_k(k_next, decltype(sc_)::value); });
-        task(IntC<B>{}, IntC<0>{}, mx, base, alpha, se, sr, ev, raise_any);
+        task(IntC<B>{}, IntC<0>{}, mx, alpha, se, sr, ev, raise_any);
         __builtin_amdgcn_sched_barrier(0);
         static_for<0, NSLOT>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
@@ -526,7 +547,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             // softmax tasks of slot i: task k (>= 1) runs in slot (k - 1) NSLOT / (NTASK - 1)
             static_for<1, NTASK>([&](auto kc) {
                 constexpr int k = decltype(kc)::value;
-                if constexpr ((k - 1) * NSLOT / (NTASK - 1) == i) task(IntC<B>{}, kc, mx, base, alpha, se, sr, ev, raise_any);
+                if constexpr ((k - 1) * NSLOT / (NTASK - 1) == i) task(IntC<B>{}, kc, mx, alpha, se, sr, ev, raise_any);
             });
             __builtin_amdgcn_sched_barrier(0);
         });
