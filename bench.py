@@ -76,9 +76,12 @@ def cpu_baseline(wl, q, k, v, budget_s=20.0):
     from exact_blockwise_attention_attn_amd.inputs import sample_rows
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        info = threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in info] or [1])
+        blas = ",".join(sorted({p.get("internal_api", "?") for p in info})) or "?"
     except Exception:  # noqa: BLE001
         threads = 1
+        blas = "?"
     rows = sample_rows(wl.N, min(wl.N, 1024), seed=12345, window=wl.window)
     mk = wl.mask_kind
     flops = 0
@@ -102,7 +105,9 @@ def cpu_baseline(wl, q, k, v, budget_s=20.0):
             w = min(wl.window, wl.N - 1)
             pairs = int(np.sum(np.minimum(rows + w, wl.N - 1) - np.maximum(rows - w, 0) + 1))
         flops += 4 * wl.d * pairs
+    full = counted_flops(wl.B, wl.H, wl.N, wl.d, wl.mask, wl.window)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "extrapolated_full_workload_s": round(elapsed * full / flops, 1), "blas": blas,
             "sample": f"{heads} of {BH} (b,h) heads x {len(rows)} seeded query rows each "
                       f"(N={wl.N}, d={wl.d}, {wl.mask}), numpy float64, {elapsed:.1f} s",
             "seconds": elapsed}
@@ -117,6 +122,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB scratch buffer between steps so every step starts with cold L2/MALL "
+                         "(steps are then timed one by one, the flush outside each)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device copy of MIB MiB per step (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -163,18 +171,39 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the kernel runs on torch's current stream; the events are recorded on that stream,
+    # one before every step and one after the last, so each step's duration is known
     stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    gpu_ms = ev0.elapsed_time(ev1)
+    scratch = torch.empty(512 << 18, dtype=torch.float32, device=dev) if args.cold else None
+    if args.cold:
+        per_step = []
+        for _ in range(args.steps):
+            scratch.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per_step.append(e0.elapsed_time(e1))
+        gpu_ms = sum(per_step)
+        wall = float("nan")
+    else:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        gpu_ms = evs[0].elapsed_time(evs[-1])
+        per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     ms_per_step = gpu_ms / args.steps
+    ms_sorted = sorted(per_step)
+    ms_median = ms_sorted[len(ms_sorted) // 2]
+    ms_min = ms_sorted[0]
     assert torch.isfinite(out).all() and torch.isfinite(lse).all(), "non-finite output"
 
     tflops = flops / (ms_per_step * 1e-3) / 1e12
@@ -196,7 +225,9 @@ def main():
         "config": {"workload": name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "mask": wl.mask,
                    "window": wl.window, "scale": wl.softmax_scale, "flops_per_step": flops,
                    "pct_of_peak": round(100.0 * tflops / peak, 2), "peak_tflops": peak,
-                   "wall_s_timed_region": round(wall, 4)},
+                   "ms_median": round(ms_median, 5), "ms_min": round(ms_min, 5),
+                   "tflops_at_median": round(flops / (ms_median * 1e-3) / 1e12, 2),
+                   "cold_l2": bool(args.cold), "wall_s_timed_region": round(wall, 4)},
         "roofline": {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": round(tflops, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": traffic,
