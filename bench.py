@@ -47,11 +47,26 @@ def algorithmic_bytes(B, H, N, d, eb):
     return 4 * B * H * N * d * eb + 4 * B * H * N
 
 
-def kernel_source_hash():
+def _code_only(text):
+    """Source text without // comments and blank lines: edits to comments leave the
+    hash (and so the recorded traffic) valid, edits to code do not."""
+    lines = []
+    for line in text.splitlines():
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            lines.append(code)
+    return "\n".join(lines)
+
+
+def kernel_source_hash(read=None):
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(rel)
+        h.update(_code_only(text).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,12 +10,11 @@
 // the end), with the running maximum that sketch leaves out (its §5.1: exp
 // overflow is the source of NaN; work relative to the maximum, in log space).
 //
-// Work decomposition.  One workgroup per (batch*head, block of BR = 32*NW query
-// rows); wave w owns 32 query rows.  The workgroup walks the key tiles (BC = 64
-// keys) that hold an allowed key for one of its rows; tiles wholly outside the
-// mask are never visited and element masking runs only on tiles that straddle the
-// mask or the sequence end.  A wave skips the matrix work of tiles that hold no
-// allowed key for its own 32 rows.
+// Work decomposition.  One workgroup of four waves (one per SIMD) per (batch*head,
+// block of BR = 256 query rows); each wave owns 64 rows (two 32-row blocks).  The
+// workgroup walks the key tiles (BC = 32 keys) that hold an allowed key for one of
+// its rows; tiles wholly outside the mask are never visited and element masking
+// runs only on tiles that straddle the mask or the sequence end.
 //
 // K/V staging.  Each K and V tile goes HBM -> LDS directly (global_load_lds_dwordx4,
 // no VGPR round trip), row-major with the 16-byte chunks of a row XOR-swizzled by
@@ -24,30 +23,33 @@
 // so every LDS read names its buffer statically and the compiler can see it never
 // aliases a load in flight into another one.
 //
-// Software pipeline.  The matrix cores compute the V product of tile t-1 while
-// the vector ALUs compute the softmax of tile t (independent streams in one basic
-// block, which the scheduler interleaves: MFMA issue between exp/fma/cvt); then
-// the scores of tile t+1.  The other wave sharing the SIMD (a second workgroup
-// per CU) fills the remaining gaps.
+// One tile as a fixed schedule.  A tile's work is three independent streams: the
+// matrix cores compute the scores of the next tile and the V product of the
+// previous one, the vector ALUs the softmax of this one, and the LDS reads fetch
+// the matrix operands a few instructions ahead.  They are laid out by hand, one
+// matrix instruction per slot with a share of the softmax behind it, and the
+// compiler's scheduler is fenced between slots, so the two kinds of work of the
+// single wave on each SIMD overlap.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, 64-wide wavefront).  Each wave
 // computes the transposed score block S^T = K_tile Q_w^T (keys x queries), so a
-// lane holds scores of ONE query (column n = lane % 32) for 32 of the 64 keys: row
+// lane holds scores of ONE query (column n = lane % 32) for 16 of the 32 keys: row
 // max and sums are in-lane plus one exchange with lane ^ 32 (v_permlane32_swap).
 // The probabilities never leave registers: the C layout of S^T, packed to bf16, is
 // the B operand of O^T += V^T P^T, where the 8 keys a lane holds per 16-key slab
 // are {4h..4h+3, 8+4h..8+4h+3} (h = lane / 32); the A operand V^T is read from the
 // row-major V tile with the transposing LDS read ds_read_b64_tr_b16 in exactly
 // that key order (a contraction index may be permuted, as long as both operands
-// agree).
+// agree).  Q sits in AGPRs for the whole kernel, read once; so does O.
 //
-// Softmax bookkeeping (log2 domain, c = |scale| log2 e): the running maximum is
-// raised only when some row of the wave grows by more than TAU (then the O
-// accumulator and sums are rescaled), so most tiles skip the rescale.  Two sums
-// are kept: the fp32 sum of the probabilities (for LSE) and the sum of the same
-// probabilities rounded to bf16 (v_dot2 with ones), which normalises O: O is then
-// an exact convex combination of V rows with the rounded weights, and the bf16
-// rounding of P perturbs relative weights only.
+// Softmax bookkeeping (log2 domain, c = |scale| log2 e).  Each row's probabilities
+// are taken against a reference m (lazily raised running maximum): a wave vote on
+// the lanes' tile maxima raises it only when some row's scores exceed m + TAU (and
+// on a row's first allowed tile), and only then are O and the sums rescaled.  Two
+// sums are kept: the fp32 sum of the probabilities (for LSE) and the sum of the
+// same probabilities rounded to bf16, which normalises O: O is then an exact convex
+// combination of V rows with the rounded weights, and the bf16 rounding of P
+// perturbs relative weights only.
 //
 // Data in HBM: q, k, v, out are contiguous [B, H, N, d] bf16, lse is [B, H, N] fp32.
 // Q is read once into registers, K and V once per query block (mostly L2/MALL
