@@ -58,6 +58,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <cstdlib>
+
 #include "attn_launch.h"
 
 namespace attn_bf16 {
@@ -559,6 +562,12 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             asm volatile("" ::"v"(l_exp[b]), "v"(l_rnd[b]));
 #pragma unroll
             for (int k = 0; k < NKS; ++k) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pr[B][b][k])));
+            // S(t+1) stays allocated at least until here, NPM matrix instructions after its
+            // last score instruction (in order, so long complete).  On the last tile its
+            // value is unused: without this the compiler could hand its registers to other
+            // values while the asm score instructions, which it cannot see into, still
+            // write them.
+            asm volatile("" : "+v"(sc[X][b][0]));
         }
         if (raise_any) rescale_o(alpha);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -619,8 +628,34 @@ static int by_mask(const AttnLaunch& a) {
 
 }  // namespace attn_bf16
 
+// Compute units of the current device (cached per device; the value never changes).
+static int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Rows per wave: 64 (two 32-row blocks: each K/V operand read feeds two matrix
+// instructions) unless that leaves the grid short of two workgroups per compute
+// unit, or the mask is a narrow band, where 32 rows per wave win: half the key tiles
+// a workgroup spans outside its band, twice the workgroups, and a register budget
+// that fits two waves per SIMD.
 int attn_launch_bf16(const AttnLaunch& a) {
     using namespace attn_bf16;
-    if (a.d == 128) return by_mask<128, 2, 1>(a);
-    return by_mask<64, 2, 1>(a);
+    const long long grid64 = (long long)((a.N + 255) / 256) * a.B * a.H;
+    const bool narrow_band = a.mask_kind == ATTN_MASK_WINDOW && 2LL * a.window + 1 < 4096 && a.window < a.N - 1;
+    bool rows32 = narrow_band || grid64 < 2LL * device_cus();
+    // explicit choice (both variants compute the same result; tests run each)
+    if (const char* f = getenv("ATTN_BF16_ROWS_PER_WAVE")) {
+        if (f[0] == '3' && f[1] == '2' && f[2] == 0) rows32 = true;
+        if (f[0] == '6' && f[1] == '4' && f[2] == 0) rows32 = false;
+    }
+    if (a.d == 128) return rows32 ? by_mask<128, 1, 1>(a) : by_mask<128, 2, 1>(a);
+    return rows32 ? by_mask<64, 1, 1>(a) : by_mask<64, 2, 1>(a);
 }

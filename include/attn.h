@@ -73,6 +73,11 @@ enum attn_status {
  * the call enqueues the work on `stream` and returns.  It keeps no state between
  * calls and may be called concurrently from several host threads.
  *
+ * Tile shape: bf16 calls pick 64 or 32 query rows per wave from the shape (32 for a
+ * grid too small to fill the device twice or a window narrower than 4096 keys);
+ * setting the environment variable ATTN_BF16_ROWS_PER_WAVE to 32 or 64 forces one.  Both
+ * compute the same result.
+ *
  * Errors: returns ATTN_OK (0) or a negative attn_status.  Argument errors are
  * detected on the host before anything is enqueued, so nothing is written on such
  * an error.  ATTN_ERR_HIP means the launch itself failed (hipGetLastError); the

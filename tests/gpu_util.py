@@ -95,7 +95,7 @@ def compare(out, lse, O_ref, L_ref, rows, dtype, label=""):
 
 
 def run_case(B, H, N, d, dtype, mask, window=0, scale=None, seed=0, q_mult=1.0, n_rows=None,
-             name="case", gen_device="cpu"):
+             name="case", gen_device="cpu", rows_per_wave=None):
     """Generate seeded inputs, run the HIP path, check against the oracle."""
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     scale = float(np.float32(scale if scale is not None else d ** -0.5))
@@ -104,8 +104,15 @@ def run_case(B, H, N, d, dtype, mask, window=0, scale=None, seed=0, q_mult=1.0, 
     say(f"[gpu] {label}")
     q, k, v = make_qkv(B, H, N, d, tdt, seed=seed, q_mult=q_mult, device=gen_device)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
-    out, lse = attn.fwd(qd, kd, vd, mask=mask, window=window, scale=scale)
-    torch.cuda.synchronize()
+    # bf16: each tile shape the library can pick (32 or 64 query rows per wave),
+    # forced in turn, against the one oracle result
+    variants = ROWS_PER_WAVE if (dtype == "bf16" and rows_per_wave is None) else (rows_per_wave,)
+    outs = []
+    for rpw in variants:
+        with forced_rows_per_wave(rpw):
+            out, lse = attn.fwd(qd, kd, vd, mask=mask, window=window, scale=scale)
+            torch.cuda.synchronize()
+        outs.append((rpw, out, lse))
     qn, kn, vn = to_np(q), to_np(k), to_np(v)
     if n_rows is None or n_rows >= N:
         rows = None
@@ -113,4 +120,32 @@ def run_case(B, H, N, d, dtype, mask, window=0, scale=None, seed=0, q_mult=1.0, 
         rows = np.stack([np.stack([sample_rows(N, n_rows, row_seed(name, seed, b, h), window)
                                    for h in range(H)]) for b in range(B)])
     O_ref, L_ref, rows = oracle(qn, kn, vn, scale, mk, window, rows)
-    return compare(out, lse, O_ref, L_ref, rows, dtype, label)
+    res = None
+    for rpw, out, lse in outs:
+        res = compare(out, lse, O_ref, L_ref, rows, dtype, f"{label} rows/wave={rpw or 'auto'}")
+    return res
+
+
+ROWS_PER_WAVE = ("32", "64")
+
+
+class forced_rows_per_wave:
+    """Context manager: force the bf16 tile shape through the library's environment
+    switch (None leaves the library's own choice)."""
+
+    def __init__(self, rpw):
+        self.rpw = rpw
+        self.old = None
+
+    def __enter__(self):
+        self.old = os.environ.get("ATTN_BF16_ROWS_PER_WAVE")
+        if self.rpw is not None:
+            os.environ["ATTN_BF16_ROWS_PER_WAVE"] = self.rpw
+        return self
+
+    def __exit__(self, *exc):
+        if self.old is None:
+            os.environ.pop("ATTN_BF16_ROWS_PER_WAVE", None)
+        else:
+            os.environ["ATTN_BF16_ROWS_PER_WAVE"] = self.old
+        return False

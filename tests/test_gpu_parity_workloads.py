@@ -17,7 +17,8 @@ def _gpu():
 def _run(name, seed=0, q_mult=1.0, n_rows=None, gen_device="cpu"):
     w = WORKLOADS[name]
     return run_case(w.B, w.H, w.N, w.d, w.dtype, w.mask, window=w.window, scale=w.softmax_scale, seed=seed,
-                    q_mult=q_mult, n_rows=n_rows, name=name, gen_device=gen_device)
+                    q_mult=q_mult, n_rows=n_rows, name=name, gen_device=gen_device,
+                    rows_per_wave="auto")   # the library's own tile choice, as bench.py runs it
 
 
 def test_tiny_f32_all_rows():

@@ -1,0 +1,91 @@
+"""The score MFMAs of the bf16 kernel are inline asm, which the compiler's hazard
+padding cannot see into.  Compile the kernel to gfx950 assembly with the build's
+flags and check, for every instantiation, that no vector-ALU instruction writes a
+source register of an asm MFMA just before it (see tests/isa_hazards.py)."""
+from __future__ import annotations
+
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+from exact_blockwise_attention_attn_amd import _build
+from tests import isa_hazards
+
+SRC = os.path.join(_build.CSRC, "attn_fwd_bf16.hip")
+
+
+def test_checker_finds_planted_hazard():
+    text = "\n".join([
+        "v_mov_b32_e32 v23, 0",
+        ";;#ASMSTART",
+        "v_mfma_f32_32x32x16_bf16 v[0:15], v[20:23], a[0:3], v[0:15]",
+        ";;#ASMEND",
+    ])
+    n, found = isa_hazards.check(text)
+    assert n == 1 and len(found) == 1
+
+
+def test_checker_finds_result_register_reused_too_early():
+    # an asm MFMA whose result the compiler thinks dead: its registers handed to a
+    # vector-ALU value while the MFMA still writes them
+    text = "\n".join([
+        ";;#ASMSTART",
+        "v_mfma_f32_32x32x16_bf16 v[16:31], v[34:37], a[80:83], 0",
+        ";;#ASMEND",
+        "s_nop 1",
+        "v_cvt_pk_bf16_f32 v16, v0, s0",
+    ])
+    n, found = isa_hazards.check(text)
+    assert n == 1 and len(found) == 1 and found[0].startswith("after")
+
+
+def test_checker_accepts_padded_result_and_chain():
+    text = "\n".join([
+        ";;#ASMSTART",
+        "v_mfma_f32_32x32x16_bf16 v[16:31], v[34:37], a[80:83], 0",
+        ";;#ASMEND",
+        ";;#ASMSTART",
+        "v_mfma_f32_32x32x16_bf16 v[16:31], v[38:41], a[84:87], v[16:31]",
+        ";;#ASMEND",
+        "s_nop 7",
+        "s_nop 7",
+        "s_nop 7",
+        "v_max_f32_e32 v40, v16, v17",
+    ])
+    assert isa_hazards.check(text) == (2, [])
+
+
+def test_checker_ignores_value_replaced_by_mfma():
+    text = "\n".join([
+        "v_or_b32_e32 v2, v6, v2",
+        ";;#ASMSTART",
+        "v_mfma_f32_32x32x16_bf16 v[0:15], v[18:21], a[80:83], 0",
+        ";;#ASMEND",
+        ";;#ASMSTART",
+        "v_mfma_f32_32x32x16_bf16 v[0:15], v[22:25], a[64:67], v[0:15]",
+        ";;#ASMEND",
+    ])
+    assert isa_hazards.check(text) == (2, [])
+
+
+@pytest.mark.skipif(shutil.which(_build.HIPCC) is None and not os.path.exists(_build.HIPCC), reason="hipcc not found")
+def test_bf16_kernel_asm_mfma_sources_not_written_by_valu():
+    with tempfile.TemporaryDirectory() as tmp:
+        out = os.path.join(tmp, "k.s")
+        cmd = [_build.HIPCC, *_build.COMMON, *_build.PER_SOURCE.get("attn_fwd_bf16.hip", []),
+               "-x", "hip", "-S", "--cuda-device-only", SRC, "-o", out]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr
+        text = open(out, encoding="utf-8").read()
+    names = re.findall(r"^(_ZN9attn_bf1610fwd_kernel\w+):", text, re.M)
+    assert len(names) == 12          # d in {64, 128} x rows per wave {32, 64} x 3 masks
+    for name in names:
+        body = text[text.index(name + ":"):]
+        body = body[:body.index("s_endpgm")]
+        n, found = isa_hazards.check(body)
+        assert n > 0, name
+        assert not found, (name, found[:3])
