@@ -301,6 +301,18 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     float m_run[QB], l_exp[QB], l_rnd[QB];     // running max (log2 domain, lazily raised), sum p, sum bf16(p)
 #pragma unroll
     for (int b = 0; b < QB; ++b) { m_run[b] = -INFINITY; l_exp[b] = 0.f; l_rnd[b] = 0.f; }
+    // At d = 64 the vector ALUs, not the matrix cores, bound a tile, so the sum of
+    // the bf16-rounded probabilities moves to the matrix cores: a product with an
+    // all-ones A operand puts each query's sum over a 16-key slab in every row of its
+    // column, so each register of a lane accumulates the full row sum (both halves).
+    constexpr bool RSM = (D == 64);
+    f32x16 lr_acc[QB];
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lr_acc[b][r] = 0.f;
+    const bf16x8 ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
+                          (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
     f32x16 sc[2][QB][KB];                      // S^T of two tiles (alternating): [query block][32-key block]
     bf16x8 pr[2][QB][NKS];                     // P^T of two tiles (alternating), [query block][16-key slab]
 
@@ -381,6 +393,11 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 for (int b = 0; b < QB; ++b)
                     o[b][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pr[X][b][ks], o[b][j], 0, 0, 0);
             }
+            if constexpr (RSM) {
+#pragma unroll
+                for (int b = 0; b < QB; ++b)
+                    lr_acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones8, pr[X][b][ks], lr_acc[b], 0, 0, 0);
+            }
         }
     };
 
@@ -394,7 +411,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // vector work runs while the matrix cores are busy instead of after them.
     constexpr int NSM = NS * QB;                 // score instructions per tile
     constexpr int NPC = NKS * ND;                // V operands per tile
-    constexpr int NPM = NPC * QB;                // V-product instructions per tile
+    constexpr int GPV = ND * QB + (RSM ? QB : 0);   // per 16-key slab: V products, then the row sums
+    constexpr int NPM = NKS * GPV;               // V-product (and row-sum) instructions per tile
     constexpr int NSLOT = NSM + NPM;
     constexpr int NEL = 16 * QB;                 // scores per lane per tile (KB = 1)
     constexpr int NTASK = QB + 1 + NEL + 1;      // lane maxima, vote, scores, sum update
@@ -463,8 +481,10 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #else
                 // sum of the rounded pair: the two bf16 halves read back as fp32
                 const uint32_t pb = __builtin_bit_cast(uint32_t, pa);
-                const float lo = __uint_as_float(pb << 16), hi = __uint_as_float(pb & 0xffff0000u);
-                sr[b] = (r == 1) ? lo + hi : sr[b] + lo + hi;
+                if constexpr (!RSM) {
+                    const float lo = __uint_as_float(pb << 16), hi = __uint_as_float(pb & 0xffff0000u);
+                    sr[b] = (r == 1) ? lo + hi : sr[b] + lo + hi;
+                }
 #endif
                 // keys 8 (r/4) + 4 hl + r % 4: slab r / 8, position r % 8
                 pr[X][b][r >> 3][(r & 7) - 1] = pa[0];
@@ -474,7 +494,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
             for (int b = 0; b < QB; ++b) {
                 l_exp[b] = __builtin_fmaf(alpha[b], l_exp[b], se[b]);
-                l_rnd[b] = __builtin_fmaf(alpha[b], l_rnd[b], sr[b]);
+                if constexpr (!RSM) l_rnd[b] = __builtin_fmaf(alpha[b], l_rnd[b], sr[b]);
             }
         }
     };
@@ -489,6 +509,10 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             for (int j = 0; j < ND; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[b][j][r] *= alpha[b];
+        if constexpr (RSM) {
+#pragma unroll
+            for (int b = 0; b < QB; ++b) lr_acc[b][0] *= alpha[b];    // the register the row sum is read from
+        }
     };
 
     // Tiles u = 0 .. n_tiles - 1 (t = t_lo + u).  K(t) lives in kbuf[u % 2], V(t) in
@@ -540,14 +564,21 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 if constexpr (s == 0) mfma_s_first(sc[X][b][0], ka[s], qreg[b][s]);
                 else mfma_s(sc[X][b][0], ka[s], qreg[b][s]);
             } else {
-                constexpr int c = (i - NSM) / QB, b = (i - NSM) % QB;
-                o[b][c % ND] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[c], pr[X][b][c / ND], o[b][c % ND], 0, 0, 0);
+                constexpr int ks = (i - NSM) / GPV, w = (i - NSM) % GPV;
+                if constexpr (w < ND * QB) {
+                    constexpr int j = w / QB, b = w % QB;
+                    o[b][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks * ND + j], pr[X][b][ks], o[b][j], 0, 0, 0);
+                } else {
+                    constexpr int b = w - ND * QB;
+                    lr_acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones8, pr[X][b][ks], lr_acc[b], 0, 0, 0);
+                }
             }
             // LDS reads for later slots
             if constexpr (i < NSM && i % QB == 0 && i / QB + KPRE < NS) ka[i / QB + KPRE] = read_k(k_next, i / QB + KPRE);
             static_for<0, NPC>([&](auto cc) {
                 constexpr int c = decltype(cc)::value;
-                if constexpr (NSM + QB * c - VLEAD == i || (i == 0 && NSM + QB * c - VLEAD < 0)) va[c] = read_v(v_prev, c);
+                constexpr int first_use = NSM + (c / ND) * GPV + (c % ND) * QB;
+                if constexpr (first_use - VLEAD == i || (i == 0 && first_use - VLEAD < 0)) va[c] = read_v(v_prev, c);
             });
             // softmax tasks of slot i: task k (>= 1) runs in slot (k - 1) NSLOT / (NTASK - 1)
             static_for<1, NTASK>([&](auto kc) {
@@ -586,7 +617,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
         const float le = swap32_add(l_exp[b]);
-        const float lr = swap32_add(l_rnd[b]);
+        const float lr = RSM ? lr_acc[b][0] : swap32_add(l_rnd[b]);
         if (my_q[b] < N) {
             const float inv = 1.0f / lr;
             __bf16* Orow = O + head + (size_t)my_q[b] * D;
