@@ -1,4 +1,4 @@
-"""Exact blockwise multi-head attention forward for MI355X (gfx950).
+"""Exact blockwise multi-head attention (forward and backward) for MI355X (gfx950).
 
 The computation runs in hand-written HIP kernels inside ``libattn.so`` behind the
 C ABI of ``include/attn.h``; this package is its Python binding.  Build the
@@ -6,7 +6,8 @@ library with ``python -m exact_blockwise_attention_attn_amd._build``.
 """
 from ._lib import (  # noqa: F401
     ATTN_DTYPE_BF16, ATTN_DTYPE_F32, ATTN_MASK_CAUSAL, ATTN_MASK_NONE, ATTN_MASK_WINDOW, ATTN_OK,
-    AttnError, LIB_PATH, attn_check_args, attn_fwd, attn_strerror, attn_version, fwd, load,
+    AttnError, LIB_PATH, attn_bwd, attn_bwd_check_args, attn_check_args, attn_fwd, attn_strerror, attn_version,
+    bwd, fwd, load,
 )
 
-__version__ = "0.1.0"
+__version__ = "0.2.0"

@@ -18,7 +18,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -34,7 +34,7 @@ COMMON = [
 # Per-source flags.  The bf16 kernel never produces or consumes NaN (masked scores
 # are -inf, every row has an allowed key), so NaN-quieting canonicalisations can go
 # and the row maximum maps onto v_max3_f32.
-PER_SOURCE = {"attn_fwd_bf16.hip": ["-fno-honor-nans"]}
+PER_SOURCE = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_bwd_bf16.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, extra: list[str]) -> str:

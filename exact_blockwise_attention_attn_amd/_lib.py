@@ -50,6 +50,10 @@ def load():
     lib.attn_fwd.restype = i
     lib.attn_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i]
     lib.attn_check_args.restype = i
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i, vp]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd_check_args.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i]
+    lib.attn_bwd_check_args.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -66,6 +70,17 @@ def attn_fwd(q, k, v, out, lse, B, H, N, d, scale, mask_kind, window, dtype, str
 def attn_check_args(q, k, v, out, lse, B, H, N, d, scale, mask_kind, window, dtype):
     """C ``attn_check_args``: host-only argument check, returns the status code."""
     return load().attn_check_args(q, k, v, out, lse, B, H, N, d, scale, mask_kind, window, dtype)
+
+
+def attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, scale, mask_kind, window, dtype, stream):
+    """C ``attn_bwd``: pointers as ints, returns the status code."""
+    return load().attn_bwd(q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, scale, mask_kind, window, dtype, stream)
+
+
+def attn_bwd_check_args(q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, scale, mask_kind, window, dtype):
+    """C ``attn_bwd_check_args``: host-only argument check, returns the status code."""
+    return load().attn_bwd_check_args(q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, scale, mask_kind, window,
+                                      dtype)
 
 
 def attn_strerror(status: int) -> str:
@@ -114,3 +129,41 @@ def fwd(q, k, v, mask="none", window=0, scale=None, out=None, lse=None, stream=N
     if st != ATTN_OK:
         raise AttnError(st, attn_strerror(st))
     return out, lse
+
+
+def bwd(q, k, v, out, dout, lse, mask="none", window=0, scale=None, dq=None, dk=None, dv=None, stream=None):
+    """Attention backward on torch device tensors: (dq, dk, dv) for the upstream
+    gradient ``dout`` of ``out``, where ``out, lse = fwd(q, k, v, mask, window,
+    scale)``.  bf16 [B, H, N, d] tensors; lse fp32 [B, H, N].  Allocates the
+    gradients unless given and enqueues on ``stream`` (default: torch's current
+    stream).  Raises AttnError on any non-zero status."""
+    import torch
+
+    ts = (q, k, v, out, dout)
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError("q, k, v, out, dout must be [B, H, N, d] tensors of one shape")
+    if any(t.dtype != torch.bfloat16 for t in ts):
+        raise ValueError("the backward takes bfloat16 tensors")
+    if not all(t.is_cuda and t.is_contiguous() for t in ts) or not (lse.is_cuda and lse.is_contiguous()):
+        raise ValueError("inputs must be contiguous device tensors")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a float32 [B, H, N] tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for g in (dq, dk, dv):
+        if g.shape != q.shape or g.dtype != q.dtype or not g.is_contiguous():
+            raise ValueError("dq, dk, dv must be contiguous tensors like q")
+    if scale is None:
+        scale = d ** -0.5
+    mk = MASKS[mask] if isinstance(mask, str) else int(mask)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), mk, int(window),
+                      ATTN_DTYPE_BF16, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, attn_strerror(st))
+    return dq, dk, dv

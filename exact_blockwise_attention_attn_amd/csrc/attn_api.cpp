@@ -72,6 +72,51 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+extern "C" int attn_bwd_check_args(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                                   const float* lse, const void* dq, const void* dk, const void* dv, int B, int H,
+                                   int N, int d, float scale, int mask_kind, int window, int dtype) {
+    if (!dout || !dq || !dk || !dv) return ATTN_ERR_NULL_PTR;
+    const int st = attn_check_args(q, k, v, out, lse, B, H, N, d, scale, mask_kind, window, dtype);
+    if (st != ATTN_OK) return st;
+    if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_BAD_DTYPE;
+    if (misaligned(dout) || misaligned(dq) || misaligned(dk) || misaligned(dv)) return ATTN_ERR_MISALIGNED;
+    const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)N;
+    const uint64_t tb = rows * (uint64_t)d * 2;
+    const uint64_t lb = rows * 4;
+    const void* ins[5] = {q, k, v, out, dout};
+    const void* outs[3] = {dq, dk, dv};
+    for (int i = 0; i < 3; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(outs[i], tb, ins[j], tb)) return ATTN_ERR_ALIAS;
+        if (overlaps(outs[i], tb, lse, lb)) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], tb, outs[j], tb)) return ATTN_ERR_ALIAS;
+    }
+    return ATTN_OK;
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                        int mask_kind, int window, int dtype, void* stream) {
+    const int st = attn_bwd_check_args(q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, scale, mask_kind, window,
+                                       dtype);
+    if (st != ATTN_OK) return st;
+    AttnBwdLaunch a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    const double c = std::fabs((double)scale) * 1.4426950408889634074;
+    a.c_log2 = (float)(c > 1e-30 ? c : 1e-30);
+    a.negate_q = scale < 0.f ? 1 : 0;
+    a.scale = scale;
+    a.mask_kind = mask_kind;
+    a.window = mask_kind == ATTN_MASK_WINDOW ? (window < N - 1 ? window : N - 1) : 0;
+    a.stream = stream;
+    (void)hipGetLastError();
+    attn_launch_bwd_bf16(a);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 extern "C" const char* attn_strerror(int status) {
     switch (status) {
         case ATTN_OK: return "success";
@@ -79,8 +124,8 @@ extern "C" const char* attn_strerror(int status) {
         case ATTN_ERR_BAD_SHAPE: return "bad shape: B, H, N must be >= 1 and within the size limits";
         case ATTN_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (d must be 64 or 128)";
         case ATTN_ERR_BAD_MASK: return "bad mask: unknown mask kind or negative window";
-        case ATTN_ERR_BAD_DTYPE: return "bad dtype (0 = fp32, 1 = bf16)";
-        case ATTN_ERR_ALIAS: return "out or lse overlaps an input or each other";
+        case ATTN_ERR_BAD_DTYPE: return "bad dtype (0 = fp32, 1 = bf16; the backward takes bf16 only)";
+        case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
         case ATTN_ERR_BAD_SCALE: return "scale is not finite";
         case ATTN_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
         case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
@@ -89,5 +134,5 @@ extern "C" const char* attn_strerror(int status) {
 }
 
 extern "C" const char* attn_version(void) {
-    return "attn 0.1.0 (gfx950; bf16 v_mfma_f32_32x32x16_bf16, fp32 VALU)";
+    return "attn 0.2.0 (gfx950; forward bf16 v_mfma_f32_32x32x16_bf16 and fp32 VALU; backward bf16)";
 }

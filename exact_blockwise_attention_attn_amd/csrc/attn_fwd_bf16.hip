@@ -62,31 +62,13 @@
 #include <cstdlib>
 
 #include "attn_launch.h"
+#include "attn_tile.h"
 
 namespace attn_bf16 {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+using namespace attn_tile;
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-
-template <int V>
-struct IntC { static constexpr int value = V; };
-constexpr float TAU = 8.0f;
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(IntC<I>{});
-        static_for<I + 1, N>(f);
-    }
-}         // lazy rescale threshold (log2 domain)
+constexpr float TAU = 8.0f;         // lazy rescale threshold (log2 domain)
 
 // Tile shape: a wave owns QB blocks of 32 query rows; a key tile is KB blocks of
 // 32 keys.  Each K or V operand read from LDS feeds QB matrix instructions.
@@ -105,31 +87,6 @@ struct Cfg {
     static_assert(TILE_BYTES % (1024 * NW) == 0, "tile must split evenly over the waves");
     static_assert(D == 64 || D == 128, "head dim");
 };
-
-// LDS layout of a K or V tile (BC rows x D/8 16-byte chunks).  Chunks are grouped
-// four at a time (64 bytes of a row); group J holds the chunks 4J..4J+3 of every
-// row contiguously, row after row, and inside a row the four chunks are XOR-ed
-// with (row / 4) mod 4:
-//     slot(row, c) = (c / 4) * 4 BC + 4 row + ((c mod 4) ^ ((row / 4) mod 4))
-// One 1 KB load instruction fills 16 rows of one group (64 contiguous bytes of
-// each row: coalesced).  Both LDS read patterns are conflict-free on 64 banks:
-// 16 consecutive rows at one chunk (K operand, 16-byte reads) and 4 consecutive
-// rows x 4 chunks of a group (V operand, transposing 8-byte reads), and every read
-// address is a per-lane base plus compile-time offsets.
-template <int BC>
-__device__ __forceinline__ int slot_of(int row, int c) {
-    return (c >> 2) * (4 * BC) + 4 * row + ((c & 3) ^ ((row >> 2) & 3));
-}
-
-__device__ __forceinline__ float swap32_max(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float swap32_add(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 template <int MASK>
 __device__ __forceinline__ bool key_allowed(int qi, int kj, int N, int window) {
@@ -153,11 +110,6 @@ __device__ __forceinline__ void tile_range(int r0, int r1, int N, int window, in
         lo = 0;
         hi = last;
     }
-}
-
-__device__ __forceinline__ bf16x4 lds_read_tr(const char* lds_base, int byte_off) {
-    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_base + byte_off));
-    return __builtin_bit_cast(bf16x4, r);
 }
 
 // Score MFMAs with the read-only Q operands pinned to the AGPR file

@@ -17,5 +17,25 @@ struct AttnLaunch {
     void* stream;
 };
 
+struct AttnBwdLaunch {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const void* dout;
+    const float* lse;
+    void* dq;
+    void* dk;
+    void* dv;
+    int B, H, N, d;
+    float c_log2;      // |scale| * log2(e), floored at 1e-30
+    int negate_q;      // scale < 0: the kernels negate the register-resident q or k and use |scale|
+    float scale;       // the signed scale, applied to dq and dk at the end
+    int mask_kind;
+    int window;        // clamped to [0, N-1]
+    void* stream;
+};
+
 int attn_launch_bf16(const AttnLaunch& a);
+int attn_launch_bwd_bf16(const AttnBwdLaunch& a);
 int attn_launch_f32(const AttnLaunch& a);

@@ -1,0 +1,86 @@
+// Shared pieces of the bf16 attention kernels (forward and backward): vector
+// types, compile-time loops, the LDS layout of a 32-row operand tile and the LDS
+// and cross-lane primitives the matrix-core mappings rely on.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn_tile {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int V>
+struct IntC { static constexpr int value = V; };
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(IntC<I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// LDS layout of a tile of BC rows x D/8 16-byte chunks (K, V, Q or dO rows).
+// Chunks are grouped four at a time (64 bytes of a row); group J holds the chunks
+// 4J..4J+3 of every row contiguously, row after row, and inside a row the four
+// chunks are XOR-ed with (row / 4) mod 4:
+//     slot(row, c) = (c / 4) * 4 BC + 4 row + ((c mod 4) ^ ((row / 4) mod 4))
+// One 1 KB load instruction fills 16 rows of one group (64 contiguous bytes of
+// each row: coalesced).  Both LDS read patterns are conflict-free on 64 banks:
+// 16 consecutive rows at one chunk (row operand, 16-byte reads) and 4 consecutive
+// rows x 4 chunks of a group (transposed operand, transposing 8-byte reads), and
+// every read address is a per-lane base plus compile-time offsets.
+template <int BC>
+__device__ __forceinline__ int slot_of(int row, int c) {
+    return (c >> 2) * (4 * BC) + 4 * row + ((c & 3) ^ ((row >> 2) & 3));
+}
+
+__device__ __forceinline__ float swap32_max(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float swap32_add(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const char* lds_base, int byte_off) {
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_base + byte_off));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// Per-lane byte offsets of the two LDS read patterns of a 32-row tile (BC = 32)
+// in the layout above, for v_mfma_f32_32x32x16_bf16 operands:
+//   row operand, slab s (16 columns): lane reads row lane % 32, columns
+//     16 s + 8 (lane / 32) .. +8  at  (s / 2) * 4 BC * 16 + (s odd ? odd : even)
+//   transposed operand (A of a product over the rows), 32-column block j and
+//     16-row slab ks: two 8-byte transposing reads at
+//     j * 4 BC * 16 + ks * 16 * 4 * 16 + tr[0] and + tr[1]; the 8 rows a lane
+//     gets per slab are {4h..4h+3, 8+4h..8+4h+3} (h = lane / 32), the order in
+//     which the C layout of a 32 x 32 product holds its rows.
+struct TileOffsets {
+    int row_even, row_odd, tr[2];
+    __device__ __forceinline__ explicit TileOffsets(int lane) {
+        const int hl = lane >> 5, ln = lane & 31;
+        const int sw = (ln >> 2) & 3;
+        row_even = (4 * ln + (hl ^ sw)) * 16;
+        row_odd = (4 * ln + ((2 + hl) ^ sw)) * 16;
+        const int g = lane >> 4, s16 = lane & 15;
+        const int k = 2 * (g & 1) + ((s16 & 3) >> 1);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            tr[r] = ((8 * r + 4 * hl + (s16 >> 2)) * 4 + (k ^ (2 * r + hl))) * 16 + (s16 & 1) * 8;
+    }
+};
+
+}  // namespace attn_tile

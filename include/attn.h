@@ -43,7 +43,7 @@ enum attn_status {
     ATTN_ERR_UNSUPPORTED_HEAD_DIM = -3,  /* d not in {64, 128}                              */
     ATTN_ERR_BAD_MASK = -4,              /* unknown mask_kind, or window < 0 for WINDOW     */
     ATTN_ERR_BAD_DTYPE = -5,             /* dtype not an attn_dtype                         */
-    ATTN_ERR_ALIAS = -6,                 /* out or lse overlaps q, k, v or each other       */
+    ATTN_ERR_ALIAS = -6,                 /* an output overlaps an input or another output   */
     ATTN_ERR_BAD_SCALE = -7,             /* scale is NaN or infinite                        */
     ATTN_ERR_MISALIGNED = -8,            /* a tensor pointer is not 16-byte aligned         */
     ATTN_ERR_HIP = -9                    /* the HIP runtime reported an error at launch     */
@@ -95,6 +95,50 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
  */
 int attn_check_args(const void* q, const void* k, const void* v, const void* out, const float* lse,
                     int B, int H, int N, int d, float scale, int mask_kind, int window, int dtype);
+
+/*
+ * attn_bwd - gradients of the attention forward: dq, dk, dv for an upstream dout.
+ *
+ * For O = softmax(scale Q K^T) V with the mask of attn_fwd, and L any scalar with
+ * dL/dO = dout, computes dq = dL/dq, dk = dL/dk, dv = dL/dv:
+ *     dV = P^T dO,  dP = dO V^T,  D_i = <dO_i, O_i>,  dS = P o (dP - D),
+ *     dQ = scale dS K,  dK = scale dS^T Q,
+ * the derivative of the forward map (masked keys excluded).  P is recomputed from
+ * q, k and the forward's lse rather than stored: the recomputation in the backward
+ * pass that the "长序列推理中的注意力机制优化策略与实践" page describes for FlashAttention
+ * (§3.1), which keeps memory O(N) like the gradient checkpointing of the Mosaic
+ * long-sequence attention page (§2.2).
+ *
+ *   q, k, v, out, dout  device pointers, contiguous [B, H, N, d] bf16; read only.
+ *             out and lse must be what attn_fwd returned for these q, k, v, scale
+ *             and mask (they define P and D).
+ *   lse       device pointer, contiguous [B, H, N] fp32 (attn_fwd's output); read only.
+ *   dq, dk, dv  device pointers, contiguous [B, H, N, d] bf16; fully overwritten.
+ *             dq also serves as the scratch for D between the three kernels the
+ *             call enqueues, so its contents are undefined until the stream
+ *             reaches the end of the call.
+ *   B, H, N, d, scale, mask_kind, window  as for attn_fwd.
+ *   dtype     ATTN_DTYPE_BF16 (fp32 inputs are not supported by the backward:
+ *             ATTN_ERR_BAD_DTYPE).  Products on bf16 matrix cores with fp32
+ *             accumulation; P and dS are rounded to bf16 for the products that
+ *             consume them; the outputs are rounded to bf16 (nearest-even).
+ *   stream    a hipStream_t (NULL = the default stream) on the current device.
+ *
+ * Ownership and errors as for attn_fwd: the library allocates nothing; argument
+ * errors (including any of dq, dk, dv overlapping an input or each other) are
+ * reported before anything is enqueued.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int mask_kind, int window,
+             int dtype, void* stream);
+
+/*
+ * attn_bwd_check_args - the host-side argument check attn_bwd performs, on its own
+ * (same arguments minus the stream; pointers are compared, never dereferenced).
+ */
+int attn_bwd_check_args(const void* q, const void* k, const void* v, const void* out, const void* dout,
+                        const float* lse, const void* dq, const void* dk, const void* dv, int B, int H, int N,
+                        int d, float scale, int mask_kind, int window, int dtype);
 
 /* attn_strerror - static, NUL-terminated text for a status code (never NULL). */
 const char* attn_strerror(int status);

@@ -21,7 +21,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["attn_check_args", "attn_fwd", "attn_strerror", "attn_version"]
+    assert declared_functions() == ["attn_bwd", "attn_bwd_check_args", "attn_check_args", "attn_fwd",
+                                    "attn_strerror", "attn_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -105,3 +106,60 @@ def test_fwd_rejects_before_launch():
 def test_binding_names_match_c_symbols():
     for name in declared_functions():
         assert callable(getattr(attn, name))
+
+
+
+# ---- backward: argument checks on fake, aligned, non-overlapping addresses
+def bwd_ptrs():
+    return [BASE + i * GAP for i in range(9)]
+
+
+def bcheck(**kw):
+    q, k, v, o, do, l, dq, dk, dv = bwd_ptrs()
+    a = dict(q=q, k=k, v=v, out=o, dout=do, lse=l, dq=dq, dk=dk, dv=dv, B=2, H=4, N=100, d=128, scale=0.1,
+             mask_kind=1, window=0, dtype=1)
+    a.update(kw)
+    return attn.attn_bwd_check_args(a["q"], a["k"], a["v"], a["out"], a["dout"], a["lse"], a["dq"], a["dk"],
+                                    a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"], a["mask_kind"],
+                                    a["window"], a["dtype"])
+
+
+def test_bwd_valid_arguments_pass():
+    assert bcheck() == _lib.ATTN_OK
+    assert bcheck(mask_kind=2, window=7, d=64) == _lib.ATTN_OK
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv"])
+def test_bwd_null_pointer(name):
+    assert bcheck(**{name: 0}) == _lib.ATTN_ERR_NULL_PTR
+
+
+def test_bwd_fp32_rejected():
+    assert bcheck(dtype=0) == _lib.ATTN_ERR_BAD_DTYPE
+
+
+@pytest.mark.parametrize("grad", ["dq", "dk", "dv"])
+@pytest.mark.parametrize("other", ["q", "k", "v", "out", "dout", "lse"])
+def test_bwd_gradient_aliasing_an_input(grad, other):
+    p = dict(zip(["q", "k", "v", "out", "dout", "lse", "dq", "dk", "dv"], bwd_ptrs()))
+    assert bcheck(**{grad: p[other] + 64}) == _lib.ATTN_ERR_ALIAS
+
+
+def test_bwd_gradients_aliasing_each_other():
+    p = bwd_ptrs()
+    assert bcheck(dk=p[6]) == _lib.ATTN_ERR_ALIAS
+    assert bcheck(dv=p[7] + 16) == _lib.ATTN_ERR_ALIAS
+
+
+def test_bwd_misaligned_and_shape():
+    assert bcheck(dq=BASE + 6 * GAP + 8) == _lib.ATTN_ERR_MISALIGNED
+    assert bcheck(N=0) == _lib.ATTN_ERR_BAD_SHAPE
+    assert bcheck(d=96) == _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM
+    assert bcheck(mask_kind=2, window=-1) == _lib.ATTN_ERR_BAD_MASK
+
+
+def test_bwd_rejects_before_any_launch():
+    # an invalid call returns its status without touching a device (none exists here)
+    q, k, v, o, do, l, dq, dk, dv = bwd_ptrs()
+    st = attn.attn_bwd(q, k, v, o, do, l, dq, dk, dv, 2, 4, 100, 96, 0.1, 0, 0, 1, None)
+    assert st == _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM
