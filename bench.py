@@ -7,7 +7,11 @@ Prints one JSON line: TFLOP/s of counted FLOPs (4 B H N^2 d dense, halved for
 causal, band pairs for the window), the roofline position of the kernel and the
 CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--pass fwd|bwd]
+
+--pass bwd times the backward (attn_bwd: dq, dk, dv from dout, O and LSE) on the
+same workload instead, counted as 2.5x the forward's FLOPs (the five products of
+the backward: the recomputed scores, dP, dV, dK and dQ).
 """
 from __future__ import annotations
 
@@ -24,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, d=128 N=8192 causal"
+METRIC_BWD = "attention bwd TFLOP/s (2.5x forward FLOPs) and % of bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense bf16 MFMA; fp32 vector
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -128,12 +133,40 @@ def cpu_baseline(wl, q, k, v, budget_s=20.0):
             "seconds": elapsed}
 
 
+def cpu_baseline_bwd(wl, q, k, v, dout, budget_s=20.0):
+    """The backward oracle, untuned, on whole heads until about ``budget_s`` of CPU
+    time (it has no row-subset mode: a head's gradients need every row)."""
+    from oracle.attention_bwd_ref import attention_backward
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    BH = wl.B * wl.H
+    per_head = counted_flops(1, 1, wl.N, wl.d, wl.mask, wl.window) * 5 // 2
+    heads, elapsed = 0, 0.0
+    while heads < BH and elapsed < budget_s:
+        b, h = divmod(heads, wl.H)
+        args = [x[b:b + 1, h:h + 1].float().cpu().numpy() for x in (q, k, v, dout)]
+        ts = time.perf_counter()
+        attention_backward(*args, wl.softmax_scale, wl.mask_kind, wl.window)
+        elapsed += time.perf_counter() - ts
+        heads += 1
+    flops = per_head * heads
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "extrapolated_full_workload_s": round(elapsed * BH / heads, 1),
+            "sample": f"{heads} of {BH} (b,h) heads, all rows (N={wl.N}, d={wl.d}, {wl.mask}), "
+                      f"numpy float64 backward, {elapsed:.1f} s",
+            "seconds": elapsed}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -178,10 +211,26 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
     flops = counted_flops(wl.B, wl.H, wl.N, wl.d, wl.mask, wl.window)
+    if args.which == "bwd":
+        if wl.dtype != "bf16":
+            print("the backward takes bf16 workloads", file=sys.stderr)
+            sys.exit(2)
+        flops = flops * 5 // 2
     eb = 2 if wl.dtype == "bf16" else 4
 
-    def step():
+    if args.which == "bwd":
         attn.fwd(q, k, v, mask=wl.mask, window=wl.window, scale=wl.softmax_scale, out=out, lse=lse)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed + 1000)
+        dout = torch.randn(q.shape, generator=gen, device=dev).to(q.dtype)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+
+        def step():
+            attn.bwd(q, k, v, out, dout, lse, mask=wl.mask, window=wl.window, scale=wl.softmax_scale,
+                     dq=dq, dk=dk, dv=dv)
+    else:
+        def step():
+            attn.fwd(q, k, v, mask=wl.mask, window=wl.window, scale=wl.softmax_scale, out=out, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -223,9 +272,9 @@ def main():
 
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name if args.which == "fwd" else name + "/bwd")
     rec = {
-        "metric": METRIC,
+        "metric": METRIC if args.which == "fwd" else METRIC_BWD,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -252,7 +301,10 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget)
+        if args.which == "fwd":
+            rec["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget)
+        else:
+            rec["cpu_baseline"] = cpu_baseline_bwd(wl, q, k, v, dout, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
 
