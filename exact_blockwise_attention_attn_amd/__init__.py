@@ -5,7 +5,7 @@ C ABI of ``include/attn.h``; this package is its Python binding.  Build the
 library with ``python -m exact_blockwise_attention_attn_amd._build``.
 """
 from ._lib import (  # noqa: F401
-    ATTN_DTYPE_BF16, ATTN_DTYPE_F32, ATTN_MASK_CAUSAL, ATTN_MASK_NONE, ATTN_MASK_WINDOW, ATTN_OK,
+    ATTN_DTYPE_BF16, ATTN_DTYPE_F32, ATTN_MASK_CAUSAL, ATTN_MASK_CAUSAL_WINDOW, ATTN_MASK_NONE, ATTN_MASK_WINDOW, ATTN_OK,
     AttnError, LIB_PATH, attn_bwd, attn_bwd_check_args, attn_check_args, attn_fwd, attn_strerror, attn_version,
     bwd, fwd, load,
 )

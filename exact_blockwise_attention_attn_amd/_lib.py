@@ -13,7 +13,7 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 
-ATTN_MASK_NONE, ATTN_MASK_CAUSAL, ATTN_MASK_WINDOW = 0, 1, 2
+ATTN_MASK_NONE, ATTN_MASK_CAUSAL, ATTN_MASK_WINDOW, ATTN_MASK_CAUSAL_WINDOW = 0, 1, 2, 3
 ATTN_DTYPE_F32, ATTN_DTYPE_BF16 = 0, 1
 ATTN_OK = 0
 ATTN_ERR_NULL_PTR = -1
@@ -26,7 +26,8 @@ ATTN_ERR_BAD_SCALE = -7
 ATTN_ERR_MISALIGNED = -8
 ATTN_ERR_HIP = -9
 
-MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL, "window": ATTN_MASK_WINDOW}
+MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL, "window": ATTN_MASK_WINDOW,
+         "causal_window": ATTN_MASK_CAUSAL_WINDOW}
 
 _lib = None
 

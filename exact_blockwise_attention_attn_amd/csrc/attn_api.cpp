@@ -32,9 +32,10 @@ extern "C" int attn_check_args(const void* q, const void* k, const void* v, cons
     if ((uint64_t)N * (uint64_t)d >= (1ull << 31) || rows >= (1ull << 31) ||
         bh * (((uint64_t)N + 63) / 64) > (1ull << 24))
         return ATTN_ERR_BAD_SHAPE;
-    if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL && mask_kind != ATTN_MASK_WINDOW)
+    if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL && mask_kind != ATTN_MASK_WINDOW &&
+        mask_kind != ATTN_MASK_CAUSAL_WINDOW)
         return ATTN_ERR_BAD_MASK;
-    if (mask_kind == ATTN_MASK_WINDOW && window < 0) return ATTN_ERR_BAD_MASK;
+    if ((mask_kind == ATTN_MASK_WINDOW || mask_kind == ATTN_MASK_CAUSAL_WINDOW) && window < 0) return ATTN_ERR_BAD_MASK;
     if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
     if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(lse))
         return ATTN_ERR_MISALIGNED;
@@ -61,7 +62,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
     a.c_log2 = (float)(c > 1e-30 ? c : 1e-30);
     a.negate_q = scale < 0.f ? 1 : 0;
     a.mask_kind = mask_kind;
-    a.window = mask_kind == ATTN_MASK_WINDOW ? (window < N - 1 ? window : N - 1) : 0;
+    a.window = (mask_kind == ATTN_MASK_WINDOW || mask_kind == ATTN_MASK_CAUSAL_WINDOW) ? (window < N - 1 ? window : N - 1) : 0;
     a.stream = stream;
 
     (void)hipGetLastError();   // clear a stale error so the check below sees only this launch
@@ -110,7 +111,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     a.negate_q = scale < 0.f ? 1 : 0;
     a.scale = scale;
     a.mask_kind = mask_kind;
-    a.window = mask_kind == ATTN_MASK_WINDOW ? (window < N - 1 ? window : N - 1) : 0;
+    a.window = (mask_kind == ATTN_MASK_WINDOW || mask_kind == ATTN_MASK_CAUSAL_WINDOW) ? (window < N - 1 ? window : N - 1) : 0;
     a.stream = stream;
     (void)hipGetLastError();
     attn_launch_bwd_bf16(a);

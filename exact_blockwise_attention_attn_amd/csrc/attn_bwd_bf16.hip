@@ -119,6 +119,9 @@ __device__ __forceinline__ void allowed_interval(int x, int N, int window, int& 
     } else if (MASK == ATTN_MASK_WINDOW) {
         lo = max(0, x - window);
         hi = min(N - 1, x + window);
+    } else if (MASK == ATTN_MASK_CAUSAL_WINDOW) {
+        if (X_IS_KEY) { lo = x; hi = min(N - 1, x + window); }     // queries j <= i <= j + w
+        else { lo = max(0, x - window); hi = x; }                   // keys i - w <= j <= i
     }
 }
 
@@ -166,6 +169,7 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
     int t_lo = 0, t_hi = (N - 1) / BT;
     if (MASK == ATTN_MASK_CAUSAL) t_lo = k0 / BT;
     if (MASK == ATTN_MASK_WINDOW) { t_lo = max(0, k0 - window) / BT; t_hi = min(N - 1, k1 + window) / BT; }
+    if (MASK == ATTN_MASK_CAUSAL_WINDOW) { t_lo = k0 / BT; t_hi = min(N - 1, k1 + window) / BT; }
     const int n_tiles = t_hi - t_lo + 1;
 
     const TileOffsets off(lane);
@@ -342,6 +346,7 @@ void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const
     int t_lo = 0, t_hi = (N - 1) / BT;
     if (MASK == ATTN_MASK_CAUSAL) t_hi = min(t_hi, r1 / BT);
     if (MASK == ATTN_MASK_WINDOW) { t_lo = max(0, q0 - window) / BT; t_hi = min(N - 1, r1 + window) / BT; }
+    if (MASK == ATTN_MASK_CAUSAL_WINDOW) { t_lo = max(0, q0 - window) / BT; t_hi = min(t_hi, r1 / BT); }
     const int n_tiles = t_hi - t_lo + 1;
 
     const TileOffsets off(lane);
@@ -450,6 +455,7 @@ static int by_mask(const AttnBwdLaunch& a) {
     switch (a.mask_kind) {
         case ATTN_MASK_CAUSAL: return launch<D, ATTN_MASK_CAUSAL>(a);
         case ATTN_MASK_WINDOW: return launch<D, ATTN_MASK_WINDOW>(a);
+        case ATTN_MASK_CAUSAL_WINDOW: return launch<D, ATTN_MASK_CAUSAL_WINDOW>(a);
         default: return launch<D, ATTN_MASK_NONE>(a);
     }
 }

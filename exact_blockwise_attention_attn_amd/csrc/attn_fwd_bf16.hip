@@ -88,14 +88,6 @@ struct Cfg {
     static_assert(D == 64 || D == 128, "head dim");
 };
 
-template <int MASK>
-__device__ __forceinline__ bool key_allowed(int qi, int kj, int N, int window) {
-    if (kj >= N) return false;
-    if (MASK == ATTN_MASK_CAUSAL) return kj <= qi;
-    if (MASK == ATTN_MASK_WINDOW) return (qi - kj <= window) && (kj - qi <= window);
-    return true;
-}
-
 // Inclusive key-tile range (tiles of BC keys) holding an allowed key for some row of [r0, r1].
 template <int MASK, int BC>
 __device__ __forceinline__ void tile_range(int r0, int r1, int N, int window, int& lo, int& hi) {
@@ -106,6 +98,9 @@ __device__ __forceinline__ void tile_range(int r0, int r1, int N, int window, in
     } else if (MASK == ATTN_MASK_WINDOW) {
         lo = max(0, r0 - window) / BC;
         hi = min(N - 1, r1 + window) / BC;
+    } else if (MASK == ATTN_MASK_CAUSAL_WINDOW) {
+        lo = max(0, r0 - window) / BC;
+        hi = min(last, r1 / BC);
     } else {
         lo = 0;
         hi = last;
@@ -303,6 +298,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         int lo = 0, hi = N - 1;
         if (MASK == ATTN_MASK_CAUSAL) hi = qi;
         if (MASK == ATTN_MASK_WINDOW) { lo = max(0, qi - window); hi = min(N - 1, qi + window); }
+        if (MASK == ATTN_MASK_CAUSAL_WINDOW) { lo = max(0, qi - window); hi = qi; }
         key_lo[b] = lo;
         key_span[b] = hi - lo;
     }
@@ -315,6 +311,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         bool need = key0 + BC > N;
         if (MASK == ATTN_MASK_CAUSAL) need |= key0 + BC - 1 > qw0;
         if (MASK == ATTN_MASK_WINDOW) need |= (key0 < qw0 + C::RW - 1 - window) || (key0 + BC - 1 > qw0 + window);
+        if (MASK == ATTN_MASK_CAUSAL_WINDOW) need |= (key0 < qw0 + C::RW - 1 - window) || (key0 + BC - 1 > qw0);
         if (need) {
             asm volatile("" ::: "memory");   // a side effect: keeps this a branch, not selects on every tile
 #pragma unroll
@@ -605,6 +602,7 @@ static int by_mask(const AttnLaunch& a) {
     switch (a.mask_kind) {
         case ATTN_MASK_CAUSAL: return launch<D, QB, KB, ATTN_MASK_CAUSAL>(a);
         case ATTN_MASK_WINDOW: return launch<D, QB, KB, ATTN_MASK_WINDOW>(a);
+        case ATTN_MASK_CAUSAL_WINDOW: return launch<D, QB, KB, ATTN_MASK_CAUSAL_WINDOW>(a);
         default: return launch<D, QB, KB, ATTN_MASK_NONE>(a);
     }
 }
@@ -632,7 +630,8 @@ static int device_cus() {
 int attn_launch_bf16(const AttnLaunch& a) {
     using namespace attn_bf16;
     const long long grid64 = (long long)((a.N + 255) / 256) * a.B * a.H;
-    const bool narrow_band = a.mask_kind == ATTN_MASK_WINDOW && 2LL * a.window + 1 < 4096 && a.window < a.N - 1;
+    const bool narrow_band = (a.mask_kind == ATTN_MASK_WINDOW && 2LL * a.window + 1 < 4096 && a.window < a.N - 1) ||
+                             (a.mask_kind == ATTN_MASK_CAUSAL_WINDOW && a.window + 1 < 2048 && a.window < a.N - 1);
     bool rows32 = narrow_band || grid64 < 2LL * device_cus();
     // explicit choice (both variants compute the same result; tests run each)
     if (const char* f = getenv("ATTN_BF16_ROWS_PER_WAVE")) {

@@ -31,6 +31,7 @@ __device__ __forceinline__ bool key_allowed(int qi, int kj, int N, int window) {
     if (kj >= N) return false;
     if (MASK == ATTN_MASK_CAUSAL) return kj <= qi;
     if (MASK == ATTN_MASK_WINDOW) return (qi - kj <= window) && (kj - qi <= window);
+    if (MASK == ATTN_MASK_CAUSAL_WINDOW) return kj <= qi && qi - kj <= window;
     return true;
 }
 
@@ -73,6 +74,7 @@ void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const 
     int lo = 0, hi = last;
     if (MASK == ATTN_MASK_CAUSAL) hi = min(last, r1 / TK);
     if (MASK == ATTN_MASK_WINDOW) { lo = max(0, q0 - window) / TK; hi = min(N - 1, r1 + window) / TK; }
+    if (MASK == ATTN_MASK_CAUSAL_WINDOW) { lo = max(0, q0 - window) / TK; hi = min(last, r1 / TK); }
     const double c = (double)c_log2;
 
     for (int t = lo; t <= hi; ++t) {
@@ -145,6 +147,7 @@ static int by_mask(const AttnLaunch& a) {
     switch (a.mask_kind) {
         case ATTN_MASK_CAUSAL: return launch<D, ATTN_MASK_CAUSAL>(a);
         case ATTN_MASK_WINDOW: return launch<D, ATTN_MASK_WINDOW>(a);
+        case ATTN_MASK_CAUSAL_WINDOW: return launch<D, ATTN_MASK_CAUSAL_WINDOW>(a);
         default: return launch<D, ATTN_MASK_NONE>(a);
     }
 }

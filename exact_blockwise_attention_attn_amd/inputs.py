@@ -14,7 +14,7 @@ from dataclasses import dataclass
 import numpy as np
 import torch
 
-MASK_CODES = {"none": 0, "causal": 1, "window": 2}
+MASK_CODES = {"none": 0, "causal": 1, "window": 2, "causal_window": 3}
 
 
 @dataclass(frozen=True)

@@ -22,6 +22,10 @@
  *     ATTN_MASK_WINDOW  key j allowed iff |i - j| <= window, the inclusive band of
  *                       the sliding-window section ("长序列推理中的注意力机制优化策略与实践",
  *                       §2.1); clipped at both ends of the sequence.
+ *     ATTN_MASK_CAUSAL_WINDOW  key j allowed iff i - window <= j <= i: the band's
+ *                       causal half (a token sees itself and the window tokens
+ *                       before it, as an autoregressive model with a bounded KV
+ *                       cache does).
  * Every row has at least one allowed key (its own), so O and LSE are always finite
  * for finite inputs.
  */
@@ -32,7 +36,7 @@
 extern "C" {
 #endif
 
-enum attn_mask_kind { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL = 1, ATTN_MASK_WINDOW = 2 };
+enum attn_mask_kind { ATTN_MASK_NONE = 0, ATTN_MASK_CAUSAL = 1, ATTN_MASK_WINDOW = 2, ATTN_MASK_CAUSAL_WINDOW = 3 };
 
 enum attn_dtype { ATTN_DTYPE_F32 = 0, ATTN_DTYPE_BF16 = 1 };
 
@@ -61,7 +65,8 @@ enum attn_status {
  *   d         head dimension: 64 or 128.
  *   scale     softmax scale applied to q.k (1/sqrt(d) for standard attention); finite.
  *   mask_kind an attn_mask_kind.
- *   window    band half-width w >= 0; read only when mask_kind == ATTN_MASK_WINDOW.
+ *   window    band half-width w >= 0; read only for ATTN_MASK_WINDOW and
+ *             ATTN_MASK_CAUSAL_WINDOW.
  *   dtype     an attn_dtype: the element type of q, k, v and out.  bf16 inputs are
  *             multiplied on bf16 matrix cores with fp32 accumulation; the
  *             probabilities are rounded to bf16 for the P.V product; O is rounded

@@ -9,9 +9,11 @@ What it computes is the plain definition of attention, written out directly.
 For every batch b, head h and query row i (0-based, N queries and N keys):
 
   A(i)   the allowed key set
-           no mask : every key j
-           causal  : j <= i                      (diagonal included)
-           window  : |i - j| <= w                (inclusive band, clipped at the ends)
+           no mask       : every key j
+           causal        : j <= i                (diagonal included)
+           window        : |i - j| <= w          (inclusive band, clipped at the ends)
+           causal window : i - w <= j <= i       (the band's causal half: the w keys
+                                                  before a token and the token itself)
   s_ij = scale * sum_c q_ic k_jc                 for j in A(i); other keys are excluded
   m_i  = max_{j in A(i)} s_ij
   p_ij = exp(s_ij - m_i)                         (0 for j outside A(i))
@@ -53,6 +55,7 @@ import numpy as np
 MASK_NONE = 0
 MASK_CAUSAL = 1
 MASK_WINDOW = 2
+MASK_CAUSAL_WINDOW = 3
 
 
 def allowed_mask(rows: np.ndarray, n_keys: int, mask_kind: int, window: int) -> np.ndarray:
@@ -67,6 +70,10 @@ def allowed_mask(rows: np.ndarray, n_keys: int, mask_kind: int, window: int) -> 
         if window < 0:
             raise ValueError("window must be >= 0")
         return np.abs(i - j) <= window
+    if mask_kind == MASK_CAUSAL_WINDOW:
+        if window < 0:
+            raise ValueError("window must be >= 0")
+        return (j <= i) & (i - j <= window)
     raise ValueError(f"unknown mask kind {mask_kind}")
 
 

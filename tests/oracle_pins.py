@@ -14,7 +14,7 @@ import mpmath
 import numpy as np
 import torch
 
-NONE, CAUSAL, WINDOW = 0, 1, 2
+NONE, CAUSAL, WINDOW, CAUSAL_WINDOW = 0, 1, 2, 3
 
 
 def _rand(shape, seed, mult=1.0):
@@ -28,6 +28,8 @@ def _allowed(i, j, mask, w):
         return True
     if mask == CAUSAL:
         return j <= i
+    if mask == CAUSAL_WINDOW:
+        return j <= i and i - j <= w
     return abs(i - j) <= w
 
 
@@ -57,7 +59,8 @@ def brute_force_mp(q, k, v, scale, mask, w, dps=50):
 def pin_brute_force(fwd):
     cases = [(1, 1, 1, 1, NONE, 0), (1, 2, 2, 4, CAUSAL, 0), (1, 1, 3, 8, WINDOW, 1),
              (2, 1, 5, 4, WINDOW, 0), (1, 1, 16, 4, CAUSAL, 0), (1, 1, 17, 8, WINDOW, 2),
-             (1, 1, 17, 1, NONE, 0), (1, 1, 5, 4, WINDOW, 5)]
+             (1, 1, 17, 1, NONE, 0), (1, 1, 5, 4, WINDOW, 5), (1, 1, 9, 4, CAUSAL_WINDOW, 2),
+             (1, 1, 6, 3, CAUSAL_WINDOW, 0)]
     for n, (B, H, N, d, mask, w) in enumerate(cases):
         q, k, v = (_rand((B, H, N, d), 100 + 3 * n + t) for t in range(3))
         scale = 1.0 / math.sqrt(d)
@@ -79,6 +82,8 @@ def sdpa_reference(q, k, v, scale, mask, w):
         allow = torch.ones(N, N, dtype=torch.bool)
     elif mask == CAUSAL:
         allow = j <= i
+    elif mask == CAUSAL_WINDOW:
+        allow = (j <= i) & (i - j <= w)
     else:
         allow = (i - j).abs() <= w
     s32 = float(np.float32(scale))
@@ -91,7 +96,8 @@ def sdpa_reference(q, k, v, scale, mask, w):
 
 def pin_sdpa(fwd):
     cases = [(1, 2, 64, 16, NONE, 0), (2, 1, 100, 32, CAUSAL, 0), (1, 2, 97, 8, WINDOW, 7),
-             (1, 1, 33, 64, WINDOW, 0), (1, 1, 40, 16, WINDOW, 100)]
+             (1, 1, 33, 64, WINDOW, 0), (1, 1, 40, 16, WINDOW, 100), (2, 1, 77, 16, CAUSAL_WINDOW, 9),
+             (1, 1, 40, 8, CAUSAL_WINDOW, 100)]
     for n, (B, H, N, d, mask, w) in enumerate(cases):
         q, k, v = (_rand((B, H, N, d), 200 + 3 * n + t) for t in range(3))
         O, L = fwd(q, k, v, 1.0 / math.sqrt(d), mask, w)
@@ -108,7 +114,7 @@ def pin_zero_query(fwd):
     v = _rand((1, 1, N, d), 7)
     k = _rand((1, 1, N, d), 8)
     q = np.zeros((1, 1, N, d))
-    for mask in (NONE, CAUSAL, WINDOW):
+    for mask in (NONE, CAUSAL, WINDOW, CAUSAL_WINDOW):
         O, L = fwd(q, k, v, 0.3, mask, w)
         for i in range(N):
             keys = [j for j in range(N) if _allowed(i, j, mask, w)]
@@ -208,6 +214,12 @@ def pin_special_cases(fwd):
         assert np.max(np.abs(Ow - On)) <= 1e-14 and np.max(np.abs(Lw - Ln)) <= 1e-14
     Oc, _ = fwd(q, k, v, 0.7, CAUSAL, 0)
     assert np.max(np.abs(Oc[0, 0, 0] - v[0, 0, 0])) <= 1e-15
+    # the causal window: w = 0 sees only the diagonal, w >= N - 1 is plain causal
+    Ocw0, Lcw0 = fwd(q, k, v, 0.7, CAUSAL_WINDOW, 0)
+    assert np.max(np.abs(Ocw0 - v)) <= 1e-15 and np.max(np.abs(Lcw0 - L)) <= 1e-14
+    for w in (N - 1, 5 * N):
+        Ocw, _ = fwd(q, k, v, 0.7, CAUSAL_WINDOW, w)
+        assert np.max(np.abs(Ocw - Oc)) <= 1e-14
     # the last causal row sees every key
     assert np.max(np.abs(Oc[0, 0, N - 1] - On[0, 0, N - 1])) <= 1e-14
     q1, k1, v1 = q[:, :, :1], k[:, :, :1], v[:, :, :1]

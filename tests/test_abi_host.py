@@ -77,7 +77,8 @@ def test_valid_arguments_pass():
     (dict(B=1 << 16, H=1 << 15, N=1), _lib.ATTN_ERR_BAD_SHAPE),     # B*H*N = 2^31
     (dict(d=96), _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM), (dict(d=0), _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM),
     (dict(d=256), _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM),
-    (dict(mask_kind=3), _lib.ATTN_ERR_BAD_MASK), (dict(mask_kind=-1), _lib.ATTN_ERR_BAD_MASK),
+    (dict(mask_kind=4), _lib.ATTN_ERR_BAD_MASK), (dict(mask_kind=-1), _lib.ATTN_ERR_BAD_MASK),
+    (dict(mask_kind=3, window=-1), _lib.ATTN_ERR_BAD_MASK),
     (dict(mask_kind=2, window=-1), _lib.ATTN_ERR_BAD_MASK),
     (dict(dtype=2), _lib.ATTN_ERR_BAD_DTYPE),
     (dict(scale=float("nan")), _lib.ATTN_ERR_BAD_SCALE), (dict(scale=float("inf")), _lib.ATTN_ERR_BAD_SCALE),

@@ -66,6 +66,12 @@ def test_bwd_window(d, N, w):
     run_bwd(1, 2, N, d, "window", window=w, seed=N + w, label="bwd-window")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,w", [(300, 0), (300, 1), (300, 31), (300, 63), (300, 200), (300, 5000), (1000, 128)])
+def test_bwd_causal_window(d, N, w):
+    run_bwd(1, 2, N, d, "causal_window", window=w, seed=N + 3 * w, label="bwd-cwindow")
+
+
 @pytest.mark.parametrize("scale", [-0.125, 2.0, 1e-3])
 def test_bwd_scales(scale):
     run_bwd(1, 2, 200, 128, "causal", scale=scale, seed=5, label="bwd-scale")
@@ -75,7 +81,7 @@ def test_bwd_batches_heads():
     run_bwd(2, 3, 257, 128, "causal", seed=9, label="bwd-bh")
 
 
-@pytest.mark.parametrize("mask", ["none", "causal", "window"])
+@pytest.mark.parametrize("mask", ["none", "causal", "window", "causal_window"])
 def test_bwd_peaked(mask):
     run_bwd(1, 2, 700, 128, mask, window=100, seed=3, q_mult=8.0, label="bwd-peaked")
 

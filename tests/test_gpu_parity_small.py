@@ -36,6 +36,14 @@ def test_window(dtype, d, N, w):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N,w", [(300, 0), (300, 1), (300, 31), (300, 32), (300, 63), (300, 200), (300, 5000),
+                                 (1000, 128), (129, 31), (1, 0)])
+def test_causal_window(dtype, d, N, w):
+    run_case(1, 2, N, d, dtype, "causal_window", window=w, seed=N + 3 * w, name="cwindow")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_batches_and_heads(dtype):
     run_case(3, 5, 200, 64, dtype, "causal", seed=7, name="bh")
 
@@ -47,7 +55,7 @@ def test_scale_values(dtype, scale):
 
 
 @pytest.mark.parametrize("q_mult", [8.0, 32.0])
-@pytest.mark.parametrize("mask", ["none", "causal", "window"])
+@pytest.mark.parametrize("mask", ["none", "causal", "window", "causal_window"])
 def test_peaked_rows(q_mult, mask):
     # large scores: exp overflow without the running max, strong max rescaling
     run_case(1, 2, 700, 128, "bf16", mask, window=100, seed=3, q_mult=q_mult, name="peaked")

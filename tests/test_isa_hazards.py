@@ -82,7 +82,7 @@ def test_bf16_kernel_asm_mfma_sources_not_written_by_valu():
         assert res.returncode == 0, res.stderr
         text = open(out, encoding="utf-8").read()
     names = re.findall(r"^(_ZN9attn_bf1610fwd_kernel\w+):", text, re.M)
-    assert len(names) == 12          # d in {64, 128} x rows per wave {32, 64} x 3 masks
+    assert len(names) == 16          # d in {64, 128} x rows per wave {32, 64} x 4 masks
     for name in names:
         body = text[text.index(name + ":"):]
         body = body[:body.index("s_endpgm")]
