@@ -25,6 +25,7 @@ ATTN_ERR_ALIAS = -6
 ATTN_ERR_BAD_SCALE = -7
 ATTN_ERR_MISALIGNED = -8
 ATTN_ERR_HIP = -9
+ATTN_ERR_WORKSPACE = -10
 
 MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL, "window": ATTN_MASK_WINDOW,
          "causal_window": ATTN_MASK_CAUSAL_WINDOW}
@@ -55,6 +56,13 @@ def load():
     lib.attn_bwd.restype = i
     lib.attn_bwd_check_args.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, i]
     lib.attn_bwd_check_args.restype = i
+    u64 = ctypes.c_ulonglong
+    lib.attn_fwd_kv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp, u64, vp]
+    lib.attn_fwd_kv.restype = i
+    lib.attn_fwd_kv_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp, u64]
+    lib.attn_fwd_kv_check_args.restype = i
+    lib.attn_fwd_kv_workspace_size.argtypes = [i, i, i, i, i]
+    lib.attn_fwd_kv_workspace_size.restype = u64
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -82,6 +90,25 @@ def attn_bwd_check_args(q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, scale, 
     """C ``attn_bwd_check_args``: host-only argument check, returns the status code."""
     return load().attn_bwd_check_args(q, k, v, out, dout, lse, dq, dk, dv, B, H, N, d, scale, mask_kind, window,
                                       dtype)
+
+
+def attn_fwd_kv(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_offset, dtype, workspace,
+                workspace_bytes, stream):
+    """C ``attn_fwd_kv``: pointers as ints, returns the status code."""
+    return load().attn_fwd_kv(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_offset, dtype,
+                              workspace, workspace_bytes, stream)
+
+
+def attn_fwd_kv_check_args(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_offset, dtype, workspace,
+                           workspace_bytes):
+    """C ``attn_fwd_kv_check_args``: host-only argument check, returns the status code."""
+    return load().attn_fwd_kv_check_args(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_offset,
+                                         dtype, workspace, workspace_bytes)
+
+
+def attn_fwd_kv_workspace_size(B, H, Nq, Nk, d) -> int:
+    """C ``attn_fwd_kv_workspace_size``: workspace bytes ``attn_fwd_kv`` needs."""
+    return int(load().attn_fwd_kv_workspace_size(B, H, Nq, Nk, d))
 
 
 def attn_strerror(status: int) -> str:
@@ -168,3 +195,48 @@ def bwd(q, k, v, out, dout, lse, mask="none", window=0, scale=None, dq=None, dk=
     if st != ATTN_OK:
         raise AttnError(st, attn_strerror(st))
     return dq, dk, dv
+
+
+def fwd_kv(q, k, v, q_offset=None, mask="none", window=0, scale=None, out=None, lse=None, workspace=None,
+           stream=None):
+    """Attention of Nq new queries against Nk cached keys on torch device tensors:
+    q [B, H, Nq, d], k and v [B, H, Nk, d], all bf16; query row i sits at position
+    ``q_offset + i`` (default ``Nk - Nq``: the queries are the last Nq tokens).
+    Allocates ``out``, ``lse`` and the workspace unless given, enqueues on
+    ``stream`` (default: torch's current stream) and returns (out, lse).  Raises
+    AttnError on any non-zero status."""
+    import torch
+
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
+        raise ValueError("attn_fwd_kv takes bfloat16 tensors")
+    if not all(t.is_cuda and t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k, v must be contiguous device tensors")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if q_offset is None:
+        q_offset = Nk - Nq
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    need = attn_fwd_kv_workspace_size(B, H, Nq, Nk, d)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if scale is None:
+        scale = d ** -0.5
+    mk = MASKS[mask] if isinstance(mask, str) else int(mask)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = attn_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
+                         float(scale), mk, int(window), int(q_offset), ATTN_DTYPE_BF16, ws_ptr, ws_bytes, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, attn_strerror(st))
+    return out, lse

@@ -118,6 +118,92 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+namespace {
+
+// shape check of the split-KV entry points; fills the workspace need when valid
+int kv_shape(int B, int H, int Nq, int Nk, int d, int q_offset, int* n_split, int* split_len, uint64_t* ws_bytes) {
+    if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || q_offset < 0 || (int64_t)q_offset + Nq > Nk)
+        return ATTN_ERR_BAD_SHAPE;
+    if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
+    const uint64_t bh = (uint64_t)B * (uint64_t)H;
+    if ((uint64_t)Nk * (uint64_t)d >= (1ull << 31) || bh * (uint64_t)Nk >= (1ull << 31) ||
+        bh * (((uint64_t)Nq + 127) / 128) > (1ull << 24))
+        return ATTN_ERR_BAD_SHAPE;
+    attn_kv_split_plan(B, H, Nq, Nk, n_split, split_len);
+    // fp32 partial O [BH, n_split, Nq, d], then fp32 partial LSE [BH, n_split, Nq]
+    const uint64_t parts = bh * (uint64_t)*n_split * (uint64_t)Nq;
+    *ws_bytes = *n_split > 1 ? parts * (uint64_t)d * 4 + parts * 4 : 0;
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" unsigned long long attn_fwd_kv_workspace_size(int B, int H, int Nq, int Nk, int d) {
+    int ns, sl;
+    uint64_t ws;
+    if (kv_shape(B, H, Nq, Nk, d, 0, &ns, &sl, &ws) != ATTN_OK) return 0;
+    return ws;
+}
+
+extern "C" int attn_fwd_kv_check_args(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                                      int B, int H, int Nq, int Nk, int d, float scale, int mask_kind, int window,
+                                      int q_offset, int dtype, const void* workspace,
+                                      unsigned long long workspace_bytes) {
+    if (!q || !k || !v || !out || !lse) return ATTN_ERR_NULL_PTR;
+    if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_BAD_DTYPE;
+    int ns, sl;
+    uint64_t need;
+    const int st = kv_shape(B, H, Nq, Nk, d, q_offset, &ns, &sl, &need);
+    if (st != ATTN_OK) return st;
+    if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL && mask_kind != ATTN_MASK_WINDOW &&
+        mask_kind != ATTN_MASK_CAUSAL_WINDOW)
+        return ATTN_ERR_BAD_MASK;
+    if ((mask_kind == ATTN_MASK_WINDOW || mask_kind == ATTN_MASK_CAUSAL_WINDOW) && window < 0) return ATTN_ERR_BAD_MASK;
+    if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+    if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_BAD_DTYPE;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out) || misaligned(lse) ||
+        (need > 0 && misaligned(workspace)))
+        return ATTN_ERR_MISALIGNED;
+    const uint64_t bh = (uint64_t)B * (uint64_t)H;
+    const uint64_t qb = bh * (uint64_t)Nq * (uint64_t)d * 2, kb = bh * (uint64_t)Nk * (uint64_t)d * 2;
+    const uint64_t lb = bh * (uint64_t)Nq * 4;
+    const void* ins[3] = {q, k, v};
+    const uint64_t in_b[3] = {qb, kb, kb};
+    for (int j = 0; j < 3; ++j) {
+        if (overlaps(out, qb, ins[j], in_b[j]) || overlaps(lse, lb, ins[j], in_b[j])) return ATTN_ERR_ALIAS;
+        if (need > 0 && overlaps(workspace, need, ins[j], in_b[j])) return ATTN_ERR_ALIAS;
+    }
+    if (overlaps(lse, lb, out, qb)) return ATTN_ERR_ALIAS;
+    if (need > 0 && (overlaps(workspace, need, out, qb) || overlaps(workspace, need, lse, lb))) return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+extern "C" int attn_fwd_kv(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int Nq,
+                           int Nk, int d, float scale, int mask_kind, int window, int q_offset, int dtype,
+                           void* workspace, unsigned long long workspace_bytes, void* stream) {
+    const int st = attn_fwd_kv_check_args(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_offset,
+                                          dtype, workspace, workspace_bytes);
+    if (st != ATTN_OK) return st;
+    int n_split, split_len;
+    uint64_t need;
+    kv_shape(B, H, Nq, Nk, d, q_offset, &n_split, &split_len, &need);
+    AttnLaunch a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    a.B = B; a.H = H; a.N = Nq; a.d = d;
+    const double c = std::fabs((double)scale) * 1.4426950408889634074;
+    a.c_log2 = (float)(c > 1e-30 ? c : 1e-30);
+    a.negate_q = scale < 0.f ? 1 : 0;
+    a.mask_kind = mask_kind;
+    a.window = (mask_kind == ATTN_MASK_WINDOW || mask_kind == ATTN_MASK_CAUSAL_WINDOW) ? (window < Nk - 1 ? window : Nk - 1) : 0;
+    a.stream = stream;
+    float* part_o = need > 0 ? (float*)workspace : nullptr;
+    float* part_lse = need > 0 ? part_o + (uint64_t)B * H * n_split * Nq * d : nullptr;
+    (void)hipGetLastError();
+    attn_launch_kv_bf16(a, Nk, q_offset, n_split, split_len, part_o, part_lse);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 extern "C" const char* attn_strerror(int status) {
     switch (status) {
         case ATTN_OK: return "success";
@@ -125,15 +211,17 @@ extern "C" const char* attn_strerror(int status) {
         case ATTN_ERR_BAD_SHAPE: return "bad shape: B, H, N must be >= 1 and within the size limits";
         case ATTN_ERR_UNSUPPORTED_HEAD_DIM: return "unsupported head dimension (d must be 64 or 128)";
         case ATTN_ERR_BAD_MASK: return "bad mask: unknown mask kind or negative window";
-        case ATTN_ERR_BAD_DTYPE: return "bad dtype (0 = fp32, 1 = bf16; the backward takes bf16 only)";
+        case ATTN_ERR_BAD_DTYPE: return "bad dtype (0 = fp32, 1 = bf16; the backward and attn_fwd_kv take bf16 only)";
         case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
         case ATTN_ERR_BAD_SCALE: return "scale is not finite";
         case ATTN_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
         case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
+        case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_fwd_kv_workspace_size()";
         default: return "unknown status";
     }
 }
 
 extern "C" const char* attn_version(void) {
-    return "attn 0.2.0 (gfx950; forward bf16 v_mfma_f32_32x32x16_bf16 and fp32 VALU; backward bf16)";
+    return "attn 0.3.0 (gfx950; forward bf16 v_mfma_f32_32x32x16_bf16 and fp32 VALU; split-KV forward bf16; "
+           "backward bf16)";
 }

@@ -129,11 +129,26 @@ __device__ __forceinline__ void settle_v(f32x16& x) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(x));
 }
 
-template <int D, int QB, int KB, int MASK>
+// Split-KV mode (queries fewer than keys, e.g. decode against a key/value cache):
+// the keys of a (batch, head) are cut into n_split ranges of split_len keys, one
+// workgroup per (query block, range); query row i sits at position q_off + i; each
+// workgroup writes its range's normalised partial O (fp32) and log-sum-exp to a
+// workspace, merged by merge_kernel.  With one range the workgroup writes O and LSE
+// itself (every row then sees its own position, so its sum is positive).
+struct SplitArgs {
+    int Nk;            // keys per head
+    int q_off;         // position of query row 0 among the keys
+    int n_split;       // key ranges per head
+    int split_len;     // keys per range (a multiple of the tile)
+    float* part_o;     // [BH, n_split, N, D] fp32
+    float* part_lse;   // [BH, n_split, N] fp32 (-inf for a range with no allowed key)
+};
+
+template <int D, int QB, int KB, int MASK, bool SPLIT = false>
 __global__ __launch_bounds__(256, 1)
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
-                int BH, int N, int nqt, float c_log2, int negate_q, int window) {
+                int BH, int N, int nqt, float c_log2, int negate_q, int window, SplitArgs sa = SplitArgs{}) {
     using C = Cfg<D, QB, KB>;
     constexpr int BC = C::BC;
     constexpr int NS = D / 16;       // 16-dim slabs of the contraction over d
@@ -155,15 +170,29 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // varies fastest, so with BH a multiple of 8 every block of a head lands on the
     // same XCD (workgroups are dealt to the 8 XCDs round robin) and shares its L2.
     const int id = blockIdx.x;
-    const int rank = id / BH;
-    const int bh = id - rank * BH;
+    int rank, bh, split = 0;
+    if constexpr (SPLIT) {
+        rank = id / (BH * sa.n_split);
+        const int rem = id - rank * (BH * sa.n_split);
+        split = rem / BH;
+        bh = rem - split * BH;
+    } else {
+        rank = id / BH;
+        bh = id - rank * BH;
+    }
     const int qt = (MASK == ATTN_MASK_CAUSAL) ? (nqt - 1 - rank) : rank;
     const int q0 = qt * C::BR;
+    // keys: Nk per head, this workgroup's range [kb, ke); query positions offset by qoff
+    const int Nk = SPLIT ? sa.Nk : N;
+    const int qoff = SPLIT ? sa.q_off : 0;
+    const int kb = SPLIT ? split * sa.split_len : 0;
+    const int ke = SPLIT ? min(Nk, kb + sa.split_len) : N;
 
     const size_t head = (size_t)bh * N * D;
+    const size_t khead = (size_t)bh * Nk * D;
     const __bf16* Qh = Q + head;
-    const __bf16* Kh = K + head;
-    const __bf16* Vh = V + head;
+    const __bf16* Kh = K + khead;
+    const __bf16* Vh = V + khead;
 
     const int qw0 = q0 + wave * C::RW;           // first row of this wave
     int my_q[QB];                                // the query of this lane's column in each 32-row block
@@ -213,21 +242,42 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
 
     int t_lo, t_hi;
-    tile_range<MASK, BC>(q0, min(q0 + C::BR, N) - 1, N, window, t_lo, t_hi);
+    tile_range<MASK, BC>(q0 + qoff, min(q0 + C::BR, N) - 1 + qoff, Nk, window, t_lo, t_hi);
+    if constexpr (SPLIT) {
+        t_lo = max(t_lo, kb / BC);
+        t_hi = min(t_hi, (ke - 1) / BC);
+        if (t_hi < t_lo) {
+            // no allowed key for any row of this block in this range: empty partials
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                if (my_q[b] < N) {
+                    const size_t pr_row = ((size_t)bh * sa.n_split + split) * N + my_q[b];
+                    float* po = sa.part_o + pr_row * D;
+#pragma unroll
+                    for (int j = 0; j < D / 32; ++j)
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            *reinterpret_cast<float4*>(po + j * 32 + 8 * g + 4 * hl) = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (hl == 0) sa.part_lse[pr_row] = -INFINITY;
+                }
+            }
+            return;
+        }
+    }
     const int n_tiles = t_hi - t_lo + 1;
 
     // direct HBM -> LDS load of tile t of one tensor into `dst` (this wave's share)
     auto dma = [&](const __bf16* src, int t, char* dst) __attribute__((always_inline)) {
         const int key0 = t * BC;
         const char* base = reinterpret_cast<const char*>(src + (size_t)key0 * D);
-        if (key0 + BC <= N) {
+        if (key0 + BC <= Nk) {
 #pragma unroll
             for (int i = 0; i < C::LOADS_PER_WAVE; ++i)
                 __builtin_amdgcn_global_load_lds((const void*)(base + ld_off[i]),
                                                  (lds_void*)(dst + (wave * C::LOADS_PER_WAVE + i) * 1024), 16, 0, 0);
         } else {
-            // last tile: rows past the end load row N - 1 (any valid row; masked later)
-            const int rows_left = N - 1 - key0;
+            // last tile: rows past the end load the last key row (any valid row; masked later)
+            const int rows_left = Nk - 1 - key0;
 #pragma unroll
             for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
                 const int row = (int)(ld_off[i] / (2 * D));
@@ -294,11 +344,16 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     int key_lo[QB], key_span[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
-        const int qi = min(my_q[b], N - 1);
-        int lo = 0, hi = N - 1;
+        const int qi = min(my_q[b], N - 1) + qoff;        // position among the keys
+        int lo = 0, hi = Nk - 1;
         if (MASK == ATTN_MASK_CAUSAL) hi = qi;
-        if (MASK == ATTN_MASK_WINDOW) { lo = max(0, qi - window); hi = min(N - 1, qi + window); }
+        if (MASK == ATTN_MASK_WINDOW) { lo = max(0, qi - window); hi = min(Nk - 1, qi + window); }
         if (MASK == ATTN_MASK_CAUSAL_WINDOW) { lo = max(0, qi - window); hi = qi; }
+        if constexpr (SPLIT) {
+            lo = max(lo, kb);
+            hi = min(hi, ke - 1);
+            if (hi < lo) { lo = 1 << 29; hi = lo; }       // no key of the range: nothing passes the test
+        }
         key_lo[b] = lo;
         key_span[b] = hi - lo;
     }
@@ -308,10 +363,12 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     auto mask_tile = [&](auto xc, int t) __attribute__((always_inline)) {
         constexpr int X = decltype(xc)::value;
         const int key0 = t * BC;
-        bool need = key0 + BC > N;
-        if (MASK == ATTN_MASK_CAUSAL) need |= key0 + BC - 1 > qw0;
-        if (MASK == ATTN_MASK_WINDOW) need |= (key0 < qw0 + C::RW - 1 - window) || (key0 + BC - 1 > qw0 + window);
-        if (MASK == ATTN_MASK_CAUSAL_WINDOW) need |= (key0 < qw0 + C::RW - 1 - window) || (key0 + BC - 1 > qw0);
+        const int pw0 = qw0 + qoff;                       // position of the wave's first row
+        bool need = key0 + BC > Nk;
+        if (MASK == ATTN_MASK_CAUSAL) need |= key0 + BC - 1 > pw0;
+        if (MASK == ATTN_MASK_WINDOW) need |= (key0 < pw0 + C::RW - 1 - window) || (key0 + BC - 1 > pw0 + window);
+        if (MASK == ATTN_MASK_CAUSAL_WINDOW) need |= (key0 < pw0 + C::RW - 1 - window) || (key0 + BC - 1 > pw0);
+        if constexpr (SPLIT) need |= (key0 < kb) || (key0 + BC > ke);
         if (need) {
             asm volatile("" ::: "memory");   // a side effect: keeps this a branch, not selects on every tile
 #pragma unroll
@@ -567,6 +624,26 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int b = 0; b < QB; ++b) {
         const float le = swap32_add(l_exp[b]);
         const float lr = RSM ? lr_acc[b][0] : swap32_add(l_rnd[b]);
+        if (SPLIT && sa.n_split > 1) {
+            if (my_q[b] < N) {
+                // this range's partial: O normalised within the range (fp32), its LSE;
+                // a row without an allowed key here gets O = 0 and LSE = -inf
+                const size_t pr_row = ((size_t)bh * sa.n_split + split) * N + my_q[b];
+                float* po = sa.part_o + pr_row * D;
+                const float inv = lr > 0.f ? 1.0f / lr : 0.f;
+#pragma unroll
+                for (int j = 0; j < ND; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        *reinterpret_cast<float4*>(po + j * 32 + 8 * g + 4 * hl) =
+                            make_float4(o[b][j][4 * g] * inv, o[b][j][4 * g + 1] * inv, o[b][j][4 * g + 2] * inv,
+                                        o[b][j][4 * g + 3] * inv);
+                if (hl == 0)
+                    sa.part_lse[pr_row] = le > 0.f ? (m_run[b] + __builtin_amdgcn_logf(le)) * 0.69314718055994531f
+                                                   : -INFINITY;
+            }
+            continue;
+        }
         if (my_q[b] < N) {
             const float inv = 1.0f / lr;
             __bf16* Orow = O + head + (size_t)my_q[b] * D;
@@ -595,6 +672,71 @@ static int launch(const AttnLaunch& a) {
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.out, a.lse,
                        a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window);
     return 0;
+}
+
+// ---- split-KV: merge the ranges' partials of every row by their log-sum-exp:
+// LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s (the exact combination of
+// softmax pieces over disjoint key sets).  One wave per row.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
+                                                    __bf16* __restrict__ O, float* __restrict__ LSE, long long rows,
+                                                    int N, int n_split) {
+    constexpr int PL = D / 64;                         // dims per lane
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    const int lane = threadIdx.x & 63;
+    const long long bh = row / N, r = row - bh * N;
+    const float* pl = part_lse + bh * n_split * (long long)N + r;
+    float m = -INFINITY;
+    for (int s = lane; s < n_split; s += 64) m = fmaxf(m, pl[(long long)s * N]);
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
+    float l = 0.f;
+    for (int s = lane; s < n_split; s += 64) l += __expf(pl[(long long)s * N] - m);
+#pragma unroll
+    for (int k = 32; k >= 1; k >>= 1) l += __shfl_xor(l, k);
+    const float lse = m == -INFINITY ? -INFINITY : m + __logf(l);   // no allowed key anywhere
+    float acc[PL];
+#pragma unroll
+    for (int c = 0; c < PL; ++c) acc[c] = 0.f;
+    for (int s = 0; s < n_split; ++s) {
+        const float ls = pl[(long long)s * N];
+        if (ls == -INFINITY) continue;                  // empty range (its O is 0)
+        const float w = __expf(ls - lse);
+        const float* po = part_o + ((bh * n_split + s) * (long long)N + r) * D + lane * PL;
+#pragma unroll
+        for (int c = 0; c < PL; ++c) acc[c] = __builtin_fmaf(w, po[c], acc[c]);
+    }
+    __bf16* orow = O + row * D + lane * PL;
+#pragma unroll
+    for (int c = 0; c < PL; ++c) orow[c] = (__bf16)acc[c];
+    if (lane == 0) LSE[row] = lse;
+}
+
+template <int D, int MASK>
+static int launch_split(const AttnLaunch& a, const SplitArgs& sa) {
+    using C = Cfg<D, 1, 1>;
+    const int nqt = (a.N + C::BR - 1) / C::BR;
+    const long long grid = (long long)nqt * a.B * a.H * sa.n_split;
+    hipStream_t st = (hipStream_t)a.stream;
+    hipLaunchKernelGGL((fwd_kernel<D, 1, 1, MASK, true>), dim3((unsigned)grid), dim3(C::NT), 0, st,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.out, a.lse,
+                       a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window, sa);
+    if (sa.n_split == 1) return 0;
+    const long long rows = (long long)a.B * a.H * a.N;
+    hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st,
+                       sa.part_o, sa.part_lse, (__bf16*)a.out, a.lse, rows, a.N, sa.n_split);
+    return 0;
+}
+
+template <int D>
+static int by_mask_split(const AttnLaunch& a, const SplitArgs& sa) {
+    switch (a.mask_kind) {
+        case ATTN_MASK_CAUSAL: return launch_split<D, ATTN_MASK_CAUSAL>(a, sa);
+        case ATTN_MASK_WINDOW: return launch_split<D, ATTN_MASK_WINDOW>(a, sa);
+        case ATTN_MASK_CAUSAL_WINDOW: return launch_split<D, ATTN_MASK_CAUSAL_WINDOW>(a, sa);
+        default: return launch_split<D, ATTN_MASK_NONE>(a, sa);
+    }
 }
 
 template <int D, int QB, int KB>
@@ -640,4 +782,34 @@ int attn_launch_bf16(const AttnLaunch& a) {
     }
     if (a.d == 128) return rows32 ? by_mask<128, 1, 1>(a) : by_mask<128, 2, 1>(a);
     return rows32 ? by_mask<64, 1, 1>(a) : by_mask<64, 2, 1>(a);
+}
+
+// Key ranges for the split-KV path: enough workgroups to fill the 256 CUs twice, at
+// least 256 keys per range, ranges a multiple of the 32-key tile.  A function of the
+// shape alone (no device query), so the workspace size is known before any launch.
+void attn_kv_split_plan(int B, int H, int Nq, int Nk, int* n_split, int* split_len) {
+    const long long blocks = (long long)((Nq + 127) / 128) * B * H;
+    const long long want = (512LL + blocks - 1) / blocks;
+    const long long max_split = (Nk + 255) / 256;
+    long long s = want < 1 ? 1 : want;
+    if (s > max_split) s = max_split;
+    if (s < 1) s = 1;
+    long long len = (Nk + s - 1) / s;
+    len = (len + 31) / 32 * 32;
+    *split_len = (int)len;
+    *n_split = (int)((Nk + len - 1) / len);
+}
+
+int attn_launch_kv_bf16(const AttnLaunch& a, int Nk, int q_offset, int n_split, int split_len, float* part_o,
+                        float* part_lse) {
+    using namespace attn_bf16;
+    SplitArgs sa;
+    sa.Nk = Nk;
+    sa.q_off = q_offset;
+    sa.n_split = n_split;
+    sa.split_len = split_len;
+    sa.part_o = part_o;
+    sa.part_lse = part_lse;
+    if (a.d == 128) return by_mask_split<128>(a, sa);
+    return by_mask_split<64>(a, sa);
 }

@@ -39,3 +39,8 @@ struct AttnBwdLaunch {
 int attn_launch_bf16(const AttnLaunch& a);
 int attn_launch_bwd_bf16(const AttnBwdLaunch& a);
 int attn_launch_f32(const AttnLaunch& a);
+
+// split-KV forward (a.N = query rows): key ranges, then the merge of the partials
+void attn_kv_split_plan(int B, int H, int Nq, int Nk, int* n_split, int* split_len);
+int attn_launch_kv_bf16(const AttnLaunch& a, int Nk, int q_offset, int n_split, int split_len, float* part_o,
+                        float* part_lse);

@@ -74,6 +74,20 @@ def make_qkv(B, H, N, d, dtype=torch.bfloat16, seed=0, q_mult=1.0, device="cpu")
     return tuple(out)
 
 
+def make_q_kv(B, H, Nq, Nk, d, dtype=torch.bfloat16, seed=0, q_mult=1.0, device="cpu"):
+    """q [B, H, Nq, d] and k, v [B, H, Nk, d] (queries against a key/value cache),
+    drawn like ``make_qkv``: one seeded generator, in the order q, k, v."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    out = []
+    for idx, n in enumerate((Nq, Nk, Nk)):
+        x = torch.randn((B, H, n, d), generator=gen, dtype=torch.float32, device=device)
+        if idx == 0 and q_mult != 1.0:
+            x.mul_(q_mult)
+        out.append(x.to(dtype).contiguous())
+    return tuple(out)
+
+
 def forced_rows(N, window=0):
     """Rows always checked, so tile and mask boundaries are covered whatever the
     kernel's tile sizes: both ends, power-of-two boundaries and the window edges."""

@@ -50,7 +50,8 @@ enum attn_status {
     ATTN_ERR_ALIAS = -6,                 /* an output overlaps an input or another output   */
     ATTN_ERR_BAD_SCALE = -7,             /* scale is NaN or infinite                        */
     ATTN_ERR_MISALIGNED = -8,            /* a tensor pointer is not 16-byte aligned         */
-    ATTN_ERR_HIP = -9                    /* the HIP runtime reported an error at launch     */
+    ATTN_ERR_HIP = -9,                   /* the HIP runtime reported an error at launch     */
+    ATTN_ERR_WORKSPACE = -10             /* workspace NULL or smaller than required         */
 };
 
 /*
@@ -144,6 +145,68 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
 int attn_bwd_check_args(const void* q, const void* k, const void* v, const void* out, const void* dout,
                         const float* lse, const void* dq, const void* dk, const void* dv, int B, int H, int N,
                         int d, float scale, int mask_kind, int window, int dtype);
+
+/*
+ * attn_fwd_kv - attention forward for Nq new queries against Nk >= Nq cached keys.
+ *
+ * Query row i of every (b, h) sits at position p_i = q_offset + i of the key
+ * sequence (a chunk of new tokens after q_offset cached ones; decode is Nq = 1,
+ * q_offset = Nk - 1), and the masks of attn_fwd apply to positions: causal allows
+ * keys j <= p_i, the window |p_i - j| <= window, the causal window
+ * p_i - window <= j <= p_i.  The output is that of attn_fwd on the full sequence,
+ * restricted to rows q_offset .. q_offset + Nq - 1.  This is the KV-cache reading
+ * of the long-sequence inference page ("长序列推理中的注意力机制优化策略与实践", §4.1:
+ * the keys and values of earlier tokens are kept and reused); its decode case is
+ * bound by memory bandwidth, not by arithmetic ("万亿参数大模型Day-0适配实践与稀疏
+ * 注意力优化", §二, item 2).  When the query blocks alone would leave the device
+ * idle, the keys of each head are cut into ranges processed by separate
+ * workgroups, each producing a partial O and LSE, which are merged exactly:
+ * LSE = ln sum_r exp(LSE_r), O = sum_r exp(LSE_r - LSE) O_r (the blockwise
+ * combination of the Mosaic long-sequence attention page, §2.2, over key ranges).
+ *
+ *   q         device pointer, contiguous [B, H, Nq, d] bf16; read only.
+ *   k, v      device pointers, contiguous [B, H, Nk, d] bf16; read only.
+ *   out       device pointer, contiguous [B, H, Nq, d] bf16; fully overwritten.
+ *   lse       device pointer, contiguous [B, H, Nq] fp32; fully overwritten.
+ *   B, H      batch and heads, >= 1.
+ *   Nq, Nk    query rows and keys per head: 1 <= Nq, q_offset + Nq <= Nk.
+ *             Limits: Nk * d < 2^31, B * H * Nk < 2^31.
+ *   d         64 or 128.
+ *   scale, mask_kind, window  as for attn_fwd (window clamped to Nk - 1).
+ *   q_offset  position of query row 0, >= 0.
+ *   dtype     ATTN_DTYPE_BF16 (ATTN_DTYPE_F32: ATTN_ERR_BAD_DTYPE).  Arithmetic as
+ *             for attn_fwd's bf16 path; the partials are fp32.
+ *   workspace device pointer to at least attn_fwd_kv_workspace_size(B, H, Nq, Nk, d)
+ *             bytes, 16-byte aligned, owned by the caller and overlapping no
+ *             tensor argument; may be NULL when that size is 0.  Its contents
+ *             are undefined after the call; it must not be reused by other work
+ *             until the stream reaches the end of the call.
+ *   workspace_bytes  its size in bytes.
+ *   stream    a hipStream_t (NULL = the default stream) on the current device.
+ *
+ * Ownership and errors as for attn_fwd: the library allocates nothing; argument
+ * errors are reported before anything is enqueued (ATTN_ERR_WORKSPACE for a
+ * missing or short workspace).
+ */
+int attn_fwd_kv(const void* q, const void* k, const void* v, void* out, float* lse,
+                int B, int H, int Nq, int Nk, int d, float scale, int mask_kind, int window, int q_offset,
+                int dtype, void* workspace, unsigned long long workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_kv_workspace_size - bytes of workspace attn_fwd_kv needs for this shape
+ * (0 when the keys are not split).  A function of the arguments alone; returns 0
+ * for arguments attn_fwd_kv would reject as a bad shape.
+ */
+unsigned long long attn_fwd_kv_workspace_size(int B, int H, int Nq, int Nk, int d);
+
+/*
+ * attn_fwd_kv_check_args - the host-side argument check attn_fwd_kv performs, on
+ * its own (same arguments minus the stream; pointers are compared, never
+ * dereferenced).
+ */
+int attn_fwd_kv_check_args(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                           int B, int H, int Nq, int Nk, int d, float scale, int mask_kind, int window,
+                           int q_offset, int dtype, const void* workspace, unsigned long long workspace_bytes);
 
 /* attn_strerror - static, NUL-terminated text for a status code (never NULL). */
 const char* attn_strerror(int status);

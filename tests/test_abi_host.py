@@ -22,6 +22,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_check_args", "attn_check_args", "attn_fwd",
+                                    "attn_fwd_kv", "attn_fwd_kv_check_args", "attn_fwd_kv_workspace_size",
                                     "attn_strerror", "attn_version"]
 
 
@@ -39,7 +40,7 @@ def test_header_enums_match_binding():
 
 def test_version_and_strerror():
     assert "gfx950" in attn.attn_version()
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         msg = attn.attn_strerror(code)
         assert msg and msg != "unknown status"
     assert attn.attn_strerror(-100) == "unknown status"
@@ -164,3 +165,76 @@ def test_bwd_rejects_before_any_launch():
     q, k, v, o, do, l, dq, dk, dv = bwd_ptrs()
     st = attn.attn_bwd(q, k, v, o, do, l, dq, dk, dv, 2, 4, 100, 96, 0.1, 0, 0, 1, None)
     assert st == _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM
+
+
+# ---- split-KV forward (Nq queries at positions q_offset.., Nk keys): host checks
+def kv_ptrs():
+    return [BASE + i * GAP for i in range(6)]
+
+
+def kvcheck(**kw):
+    q, k, v, o, l, ws = kv_ptrs()
+    a = dict(q=q, k=k, v=v, out=o, lse=l, B=1, H=8, Nq=1, Nk=65536, d=128, scale=0.1, mask_kind=1, window=0,
+             q_offset=65535, dtype=1, workspace=ws, workspace_bytes=1 << 30)
+    a.update(kw)
+    return attn.attn_fwd_kv_check_args(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["Nq"],
+                                       a["Nk"], a["d"], a["scale"], a["mask_kind"], a["window"], a["q_offset"],
+                                       a["dtype"], a["workspace"], a["workspace_bytes"])
+
+
+def test_kv_workspace_size_shape():
+    """Partial O and LSE in fp32: B H n_split Nq (4 d + 4) bytes, with 2 <= n_split
+    <= ceil(Nk / 256) when the query blocks are too few to fill the device."""
+    for B, H, Nq, Nk, d in [(1, 8, 1, 65536, 128), (4, 32, 1, 131072, 128), (1, 1, 16, 300, 64),
+                            (2, 4, 5, 4096, 64)]:
+        ws = attn.attn_fwd_kv_workspace_size(B, H, Nq, Nk, d)
+        per = B * H * Nq * (4 * d + 4)
+        assert ws > 0 and ws % per == 0, (B, H, Nq, Nk, d, ws)
+        assert 2 <= ws // per <= -(-Nk // 256)
+    # one key range is enough once the query blocks fill the device: no workspace
+    assert attn.attn_fwd_kv_workspace_size(2, 32, 8192, 8192, 128) == 0
+    assert attn.attn_fwd_kv_workspace_size(1, 1, 1, 256, 128) == 0          # 256 keys: one range
+    # shapes attn_fwd_kv rejects
+    assert attn.attn_fwd_kv_workspace_size(1, 1, 10, 5, 128) == 0
+    assert attn.attn_fwd_kv_workspace_size(0, 1, 1, 5, 128) == 0
+    assert attn.attn_fwd_kv_workspace_size(1, 1, 1, 4096, 96) == 0
+
+
+def test_kv_valid_arguments_pass():
+    assert kvcheck() == _lib.ATTN_OK
+    assert kvcheck(mask_kind=0, q_offset=0) == _lib.ATTN_OK
+    assert kvcheck(mask_kind=2, window=100, d=64, Nq=64, q_offset=100) == _lib.ATTN_OK
+    need = attn.attn_fwd_kv_workspace_size(1, 8, 1, 65536, 128)
+    assert kvcheck(workspace_bytes=need) == _lib.ATTN_OK
+    # no workspace needed: NULL is fine
+    assert kvcheck(B=2, H=32, Nq=8192, Nk=8192, q_offset=0, workspace=0, workspace_bytes=0) == _lib.ATTN_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), _lib.ATTN_ERR_NULL_PTR), (dict(lse=0), _lib.ATTN_ERR_NULL_PTR),
+    (dict(Nq=0), _lib.ATTN_ERR_BAD_SHAPE), (dict(Nk=0), _lib.ATTN_ERR_BAD_SHAPE),
+    (dict(q_offset=-1), _lib.ATTN_ERR_BAD_SHAPE), (dict(q_offset=65536), _lib.ATTN_ERR_BAD_SHAPE),
+    (dict(Nq=2), _lib.ATTN_ERR_BAD_SHAPE),                                      # q_offset + Nq > Nk
+    (dict(Nk=1 << 24, q_offset=0), _lib.ATTN_ERR_BAD_SHAPE),                    # Nk * d = 2^31
+    (dict(d=96), _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM),
+    (dict(mask_kind=5), _lib.ATTN_ERR_BAD_MASK), (dict(mask_kind=3, window=-2), _lib.ATTN_ERR_BAD_MASK),
+    (dict(scale=float("nan")), _lib.ATTN_ERR_BAD_SCALE),
+    (dict(dtype=0), _lib.ATTN_ERR_BAD_DTYPE), (dict(dtype=7), _lib.ATTN_ERR_BAD_DTYPE),
+    (dict(workspace=0), _lib.ATTN_ERR_WORKSPACE), (dict(workspace_bytes=100), _lib.ATTN_ERR_WORKSPACE),
+    (dict(workspace=BASE + 5 * GAP + 4), _lib.ATTN_ERR_MISALIGNED),
+    (dict(k=BASE + 8), _lib.ATTN_ERR_MISALIGNED),
+    (dict(out=BASE + GAP + 1024), _lib.ATTN_ERR_ALIAS),                         # out inside k
+    (dict(workspace=BASE + 2 * GAP + 64), _lib.ATTN_ERR_ALIAS),                 # workspace inside v
+    (dict(workspace=BASE + 4 * GAP - 64), _lib.ATTN_ERR_ALIAS),                 # workspace runs into lse
+    (dict(lse=BASE + 3 * GAP + 16), _lib.ATTN_ERR_ALIAS),                       # lse inside out
+])
+def test_kv_invalid_arguments(kw, code):
+    assert kvcheck(**kw) == code
+
+
+def test_kv_rejects_before_any_launch():
+    q, k, v, o, l, ws = kv_ptrs()
+    st = attn.attn_fwd_kv(q, k, v, o, l, 1, 8, 4, 2, 128, 0.1, 0, 0, 0, 1, ws, 1 << 30, None)
+    assert st == _lib.ATTN_ERR_BAD_SHAPE
+    st = attn.attn_fwd_kv(q, k, v, o, l, 1, 8, 1, 65536, 128, 0.1, 0, 0, 0, 1, 0, 0, None)
+    assert st == _lib.ATTN_ERR_WORKSPACE
