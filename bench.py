@@ -7,11 +7,16 @@ Prints one JSON line: TFLOP/s of counted FLOPs (4 B H N^2 d dense, halved for
 causal, band pairs for the window), the roofline position of the kernel and the
 CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--pass fwd|bwd]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--pass fwd|bwd|decode]
 
 --pass bwd times the backward (attn_bwd: dq, dk, dv from dout, O and LSE) on the
 same workload instead, counted as 2.5x the forward's FLOPs (the five products of
 the backward: the recomputed scores, dP, dV, dK and dQ).
+
+--pass decode times attn_fwd_kv on a decode workload (one new query per sequence
+against a key/value cache; default B=1 H=32 Nk=131072 d=128 causal).  That work is
+bound by HBM bandwidth, so the figure is GB/s of the bytes the step must move (the
+K and V cache read once, q read, O and LSE written) against the 8 TB/s peak.
 """
 from __future__ import annotations
 
@@ -29,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, d=128 N=8192 causal"
 METRIC_BWD = "attention bwd TFLOP/s (2.5x forward FLOPs) and % of bf16 MFMA peak"
+METRIC_DECODE = "attention decode (split-KV) GB/s of K/V cache read and % of HBM peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense bf16 MFMA; fp32 vector
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -160,13 +166,103 @@ def cpu_baseline_bwd(wl, q, k, v, dout, budget_s=20.0):
             "seconds": elapsed}
 
 
+def kv_bytes(wl):
+    """Bytes one decode step must move: K and V read once, q read, O and LSE written."""
+    return 2 * wl.B * wl.H * wl.Nk * wl.d * 2 + 2 * wl.B * wl.H * wl.Nq * wl.d * 2 + 4 * wl.B * wl.H * wl.Nq
+
+
+def cpu_baseline_kv(wl, q, k, v, budget_s=20.0):
+    """The cache oracle, untuned, on whole heads until about ``budget_s`` of CPU time,
+    reported in the decode metric's unit (bytes of the heads' K/V per second)."""
+    from oracle.attention_kv_ref import attention_forward_kv
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    BH = wl.B * wl.H
+    heads, elapsed = 0, 0.0
+    while heads < BH and elapsed < budget_s:
+        b, h = divmod(heads, wl.H)
+        args = [x[b:b + 1, h:h + 1].float().cpu().numpy() for x in (q, k, v)]
+        ts = time.perf_counter()
+        attention_forward_kv(*args, wl.softmax_scale, wl.mask_kind, wl.window, wl.Nk - wl.Nq)
+        elapsed += time.perf_counter() - ts
+        heads += 1
+    moved = kv_bytes(wl) * heads / BH
+    return {"value": round(moved / elapsed / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "extrapolated_full_workload_s": round(elapsed * BH / heads, 3),
+            "sample": f"{heads} of {BH} (b,h) heads, Nq={wl.Nq} Nk={wl.Nk} d={wl.d} {wl.mask}, numpy float64, "
+                      f"{elapsed:.1f} s",
+            "seconds": elapsed}
+
+
+def main_decode(args, torch, attn):
+    from exact_blockwise_attention_attn_amd.inputs import KV_HEADLINE, KV_WORKLOADS, make_q_kv
+
+    name = args.workload or KV_HEADLINE
+    wl = KV_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v = make_q_kv(wl.B, wl.H, wl.Nq, wl.Nk, wl.d, torch.bfloat16, seed=args.seed, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.Nq), dtype=torch.float32, device=dev)
+    need = attn.attn_fwd_kv_workspace_size(wl.B, wl.H, wl.Nq, wl.Nk, wl.d)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    off = wl.Nk - wl.Nq
+
+    def step():
+        attn.fwd_kv(q, k, v, q_offset=off, mask=wl.mask, window=wl.window, scale=wl.softmax_scale, out=out,
+                    lse=lse, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    assert torch.isfinite(out).all() and torch.isfinite(lse).all(), "non-finite output"
+    moved = kv_bytes(wl)
+    gbs = moved / (ms * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC_DECODE,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) q and K/V cache drawn on the device",
+        "config": {"workload": name, "B": wl.B, "H": wl.H, "Nq": wl.Nq, "Nk": wl.Nk, "d": wl.d, "mask": wl.mask,
+                   "q_offset": off, "workspace_bytes": need, "bytes_per_step": moved,
+                   "ms_median": round(per_step[len(per_step) // 2], 5), "ms_min": round(per_step[0], 5),
+                   "wall_s_timed_region": round(wall, 4),
+                   "step": "split-range kernel + log-sum-exp merge kernel"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name)},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_kv(wl, q, k, v, args.cpu_budget),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd"], default="fwd")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "decode"], default="fwd")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -187,14 +283,17 @@ def main():
     import exact_blockwise_attention_attn_amd as attn
     from exact_blockwise_attention_attn_amd.inputs import HEADLINE, WORKLOADS, make_qkv
 
-    name = args.workload or HEADLINE
-    wl = WORKLOADS[name]
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     attn.load()
+    if args.which == "decode":
+        main_decode(args, torch, attn)
+        return
+    name = args.workload or HEADLINE
+    wl = WORKLOADS[name]
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20) // 4

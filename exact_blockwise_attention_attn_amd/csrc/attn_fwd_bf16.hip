@@ -682,6 +682,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
                                                     __bf16* __restrict__ O, float* __restrict__ LSE, long long rows,
                                                     int N, int n_split) {
     constexpr int PL = D / 64;                         // dims per lane
+    constexpr int G = 8;                               // partial rows loaded together
     const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= rows) return;
     const int lane = threadIdx.x & 63;
@@ -699,13 +700,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     float acc[PL];
 #pragma unroll
     for (int c = 0; c < PL; ++c) acc[c] = 0.f;
-    for (int s = 0; s < n_split; ++s) {
-        const float ls = pl[(long long)s * N];
-        if (ls == -INFINITY) continue;                  // empty range (its O is 0)
-        const float w = __expf(ls - lse);
-        const float* po = part_o + ((bh * n_split + s) * (long long)N + r) * D + lane * PL;
+    const float* po0 = part_o + (bh * n_split * (long long)N + r) * D + lane * PL;
+    const long long stride = (long long)N * D;         // between the ranges' partial rows
+    for (int c0 = 0; c0 < n_split; c0 += 64) {
+        // lane s holds the weight of range c0 + s (an empty range has O = 0 and weight 0)
+        const int sl = c0 + lane;
+        const float w_l = (sl < n_split && lse != -INFINITY) ? __expf(pl[(long long)sl * N] - lse) : 0.f;
+        const int cn = min(64, n_split - c0);
+        for (int g0 = 0; g0 < cn; g0 += G) {
+            float v[G][PL];
 #pragma unroll
-        for (int c = 0; c < PL; ++c) acc[c] = __builtin_fmaf(w, po[c], acc[c]);
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int c = 0; c < PL; ++c) v[g][c] = (g0 + g < cn) ? po0[(c0 + g0 + g) * stride + c] : 0.f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const float w = __shfl(w_l, g0 + g);
+#pragma unroll
+                for (int c = 0; c < PL; ++c) acc[c] = __builtin_fmaf(w, v[g][c], acc[c]);
+            }
+        }
     }
     __bf16* orow = O + row * D + lane * PL;
 #pragma unroll

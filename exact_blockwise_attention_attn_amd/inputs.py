@@ -57,6 +57,37 @@ WORKLOADS = {
 HEADLINE = "causal_bf16_b2h32_n8192_d128"
 
 
+@dataclass(frozen=True)
+class KvWorkload:
+    """Nq new queries at positions Nk - Nq .. Nk - 1 against Nk cached keys (bf16)."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    mask: str
+    window: int = 0
+
+    @property
+    def mask_kind(self) -> int:
+        return MASK_CODES[self.mask]
+
+    @property
+    def softmax_scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.d)))
+
+
+# Decode steps (one new token per sequence) with LLaMA-7B heads: one long context,
+# and a batch of eight 8K contexts.
+KV_WORKLOADS = {
+    "decode_bf16_h32_nk131072_d128": KvWorkload("decode_bf16_h32_nk131072_d128", 1, 32, 1, 131072, 128, "causal"),
+    "decode_bf16_b8h32_nk8192_d128": KvWorkload("decode_bf16_b8h32_nk8192_d128", 8, 32, 1, 8192, 128, "causal"),
+}
+
+KV_HEADLINE = "decode_bf16_h32_nk131072_d128"
+
+
 def make_qkv(B, H, N, d, dtype=torch.bfloat16, seed=0, q_mult=1.0, device="cpu"):
     """q, k, v as contiguous [B, H, N, d] tensors of ``dtype``.
 
