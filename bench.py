@@ -39,7 +39,9 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense bf16 MFMA; fp32
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["exact_blockwise_attention_attn_amd/csrc/attn_fwd_bf16.hip",
-                  "exact_blockwise_attention_attn_amd/csrc/attn_fwd_f32.hip"]
+                  "exact_blockwise_attention_attn_amd/csrc/attn_fwd_f32.hip",
+                  "exact_blockwise_attention_attn_amd/csrc/attn_bwd_bf16.hip",
+                  "exact_blockwise_attention_attn_amd/csrc/attn_tile.h"]
 
 
 def counted_flops(B, H, N, d, mask, window=0):
