@@ -41,6 +41,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["exact_blockwise_attention_attn_amd/csrc/attn_fwd_bf16.hip",
                   "exact_blockwise_attention_attn_amd/csrc/attn_fwd_f32.hip",
                   "exact_blockwise_attention_attn_amd/csrc/attn_bwd_bf16.hip",
+                  "exact_blockwise_attention_attn_amd/csrc/attn_decode_bf16.hip",
                   "exact_blockwise_attention_attn_amd/csrc/attn_tile.h"]
 
 

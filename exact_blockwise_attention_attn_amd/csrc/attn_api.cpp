@@ -121,7 +121,7 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
 namespace {
 
 // shape check of the split-KV entry points; fills the workspace need when valid
-int kv_shape(int B, int H, int Nq, int Nk, int d, int q_offset, int* n_split, int* split_len, uint64_t* ws_bytes) {
+int kv_shape(int B, int H, int Nq, int Nk, int d, int q_offset, int* n_split, uint64_t* ws_bytes) {
     if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || q_offset < 0 || (int64_t)q_offset + Nq > Nk)
         return ATTN_ERR_BAD_SHAPE;
     if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED_HEAD_DIM;
@@ -129,8 +129,9 @@ int kv_shape(int B, int H, int Nq, int Nk, int d, int q_offset, int* n_split, in
     if ((uint64_t)Nk * (uint64_t)d >= (1ull << 31) || bh * (uint64_t)Nk >= (1ull << 31) ||
         bh * (((uint64_t)Nq + 127) / 128) > (1ull << 24))
         return ATTN_ERR_BAD_SHAPE;
-    attn_kv_split_plan(B, H, Nq, Nk, n_split, split_len);
-    // fp32 partial O [BH, n_split, Nq, d], then fp32 partial LSE [BH, n_split, Nq]
+    // fp32 partial O [BH, splits, Nq, d], then fp32 partial LSE [BH, splits, Nq], for the
+    // most ranges a launch of this shape can use
+    *n_split = attn_kv_max_splits(B, H, Nq, Nk, d);
     const uint64_t parts = bh * (uint64_t)*n_split * (uint64_t)Nq;
     *ws_bytes = *n_split > 1 ? parts * (uint64_t)d * 4 + parts * 4 : 0;
     return ATTN_OK;
@@ -139,9 +140,9 @@ int kv_shape(int B, int H, int Nq, int Nk, int d, int q_offset, int* n_split, in
 }  // namespace
 
 extern "C" unsigned long long attn_fwd_kv_workspace_size(int B, int H, int Nq, int Nk, int d) {
-    int ns, sl;
+    int ns;
     uint64_t ws;
-    if (kv_shape(B, H, Nq, Nk, d, 0, &ns, &sl, &ws) != ATTN_OK) return 0;
+    if (kv_shape(B, H, Nq, Nk, d, 0, &ns, &ws) != ATTN_OK) return 0;
     return ws;
 }
 
@@ -151,9 +152,9 @@ extern "C" int attn_fwd_kv_check_args(const void* q, const void* k, const void* 
                                       unsigned long long workspace_bytes) {
     if (!q || !k || !v || !out || !lse) return ATTN_ERR_NULL_PTR;
     if (dtype != ATTN_DTYPE_F32 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_BAD_DTYPE;
-    int ns, sl;
+    int ns;
     uint64_t need;
-    const int st = kv_shape(B, H, Nq, Nk, d, q_offset, &ns, &sl, &need);
+    const int st = kv_shape(B, H, Nq, Nk, d, q_offset, &ns, &need);
     if (st != ATTN_OK) return st;
     if (mask_kind != ATTN_MASK_NONE && mask_kind != ATTN_MASK_CAUSAL && mask_kind != ATTN_MASK_WINDOW &&
         mask_kind != ATTN_MASK_CAUSAL_WINDOW)
@@ -185,9 +186,9 @@ extern "C" int attn_fwd_kv(const void* q, const void* k, const void* v, void* ou
     const int st = attn_fwd_kv_check_args(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_offset,
                                           dtype, workspace, workspace_bytes);
     if (st != ATTN_OK) return st;
-    int n_split, split_len;
+    int n_split;
     uint64_t need;
-    kv_shape(B, H, Nq, Nk, d, q_offset, &n_split, &split_len, &need);
+    kv_shape(B, H, Nq, Nk, d, q_offset, &n_split, &need);
     AttnLaunch a;
     a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
     a.B = B; a.H = H; a.N = Nq; a.d = d;
@@ -200,7 +201,7 @@ extern "C" int attn_fwd_kv(const void* q, const void* k, const void* v, void* ou
     float* part_o = need > 0 ? (float*)workspace : nullptr;
     float* part_lse = need > 0 ? part_o + (uint64_t)B * H * n_split * Nq * d : nullptr;
     (void)hipGetLastError();
-    attn_launch_kv_bf16(a, Nk, q_offset, n_split, split_len, part_o, part_lse);
+    attn_launch_kv_bf16(a, Nk, q_offset, part_o, part_lse);
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 

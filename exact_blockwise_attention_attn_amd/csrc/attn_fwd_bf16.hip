@@ -825,14 +825,40 @@ void attn_kv_split_plan(int B, int H, int Nq, int Nk, int* n_split, int* split_l
     *n_split = (int)((Nk + len - 1) / len);
 }
 
-int attn_launch_kv_bf16(const AttnLaunch& a, int Nk, int q_offset, int n_split, int split_len, float* part_o,
-                        float* part_lse) {
+int attn_kv_max_splits(int B, int H, int Nq, int Nk, int d) {
+    if (Nq == 1) return attn_decode_max_splits(B * H, Nk, d);
+    int n_split, split_len;
+    attn_kv_split_plan(B, H, Nq, Nk, &n_split, &split_len);
+    return n_split;
+}
+
+int attn_launch_kv_bf16(const AttnLaunch& a, int Nk, int q_offset, float* part_o, float* part_lse) {
     using namespace attn_bf16;
+    if (a.N == 1) {
+        // decode: the query's allowed keys are one interval
+        const int p = q_offset;
+        int lo = 0, hi = Nk - 1;
+        if (a.mask_kind == ATTN_MASK_CAUSAL) hi = p;
+        if (a.mask_kind == ATTN_MASK_WINDOW) { lo = max(0, p - a.window); hi = min(Nk - 1, p + a.window); }
+        if (a.mask_kind == ATTN_MASK_CAUSAL_WINDOW) { lo = max(0, p - a.window); hi = p; }
+        int n_split = 1;
+        attn_launch_decode_bf16(a, Nk, lo, hi, part_o, part_lse, &n_split);
+        if (n_split > 1) {
+            const long long rows = (long long)a.B * a.H;
+            hipStream_t st = (hipStream_t)a.stream;
+            if (a.d == 128)
+                hipLaunchKernelGGL((merge_kernel<128>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, part_o,
+                                   part_lse, (__bf16*)a.out, a.lse, rows, 1, n_split);
+            else
+                hipLaunchKernelGGL((merge_kernel<64>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, st, part_o,
+                                   part_lse, (__bf16*)a.out, a.lse, rows, 1, n_split);
+        }
+        return 0;
+    }
     SplitArgs sa;
+    attn_kv_split_plan(a.B, a.H, a.N, Nk, &sa.n_split, &sa.split_len);
     sa.Nk = Nk;
     sa.q_off = q_offset;
-    sa.n_split = n_split;
-    sa.split_len = split_len;
     sa.part_o = part_o;
     sa.part_lse = part_lse;
     if (a.d == 128) return by_mask_split<128>(a, sa);

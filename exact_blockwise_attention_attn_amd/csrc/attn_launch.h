@@ -40,7 +40,14 @@ int attn_launch_bf16(const AttnLaunch& a);
 int attn_launch_bwd_bf16(const AttnBwdLaunch& a);
 int attn_launch_f32(const AttnLaunch& a);
 
-// split-KV forward (a.N = query rows): key ranges, then the merge of the partials
+// split-KV forward (a.N = query rows): key ranges, then the merge of the partials.
+// attn_kv_max_splits bounds the ranges any launch of the shape uses (it sizes the
+// workspace: fp32 partial O [B*H, splits, Nq, d], then partial LSE [B*H, splits, Nq]).
 void attn_kv_split_plan(int B, int H, int Nq, int Nk, int* n_split, int* split_len);
-int attn_launch_kv_bf16(const AttnLaunch& a, int Nk, int q_offset, int n_split, int split_len, float* part_o,
-                        float* part_lse);
+int attn_kv_max_splits(int B, int H, int Nq, int Nk, int d);
+int attn_launch_kv_bf16(const AttnLaunch& a, int Nk, int q_offset, float* part_o, float* part_lse);
+
+// decode (one query per head): the key interval [lo, hi] in ranges, one workgroup each
+int attn_decode_max_splits(int BH, int Nk, int d);
+int attn_launch_decode_bf16(const AttnLaunch& a, int Nk, int lo, int hi, float* part_o, float* part_lse,
+                            int* n_split_used);

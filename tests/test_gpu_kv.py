@@ -74,6 +74,13 @@ def test_decode_window(d, mask, Nk, w):
     run_kv(1, 4, 1, Nk, d, mask, window=w, seed=Nk + w, name="decode_w")
 
 
+@pytest.mark.parametrize("B,H,Nk,d", [(1, 1024, 600, 64), (1, 700, 1500, 128), (2, 3, 100000, 64)])
+def test_decode_many_heads_and_ranges(B, H, Nk, d):
+    """Decode with more heads than one round of workgroups (one key range: the
+    kernel writes O and LSE itself), with two ranges per head, and with many."""
+    run_kv(B, H, 1, Nk, d, "causal", seed=H + Nk, name="decode_heads")
+
+
 @pytest.mark.parametrize("mask,w", [("none", 0), ("causal", 0), ("window", 37), ("window", 300),
                                     ("causal_window", 0), ("causal_window", 100)])
 @pytest.mark.parametrize("Nq,off", [(5, 0), (5, 2000), (5, 2995), (64, 1000), (129, 0), (129, 2871), (300, 700)])
