@@ -38,11 +38,13 @@ METRIC_DECODE = "attention decode (split-KV) GB/s of K/V cache read and % of HBM
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense bf16 MFMA; fp32 vector
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["exact_blockwise_attention_attn_amd/csrc/attn_fwd_bf16.hip",
-                  "exact_blockwise_attention_attn_amd/csrc/attn_fwd_f32.hip",
-                  "exact_blockwise_attention_attn_amd/csrc/attn_bwd_bf16.hip",
-                  "exact_blockwise_attention_attn_amd/csrc/attn_decode_bf16.hip",
-                  "exact_blockwise_attention_attn_amd/csrc/attn_tile.h"]
+CSRC = "exact_blockwise_attention_attn_amd/csrc/"
+# the sources each measured workload runs: a traffic record stays valid while they are unchanged
+KERNEL_SOURCES = {
+    "fwd": [CSRC + "attn_fwd_bf16.hip", CSRC + "attn_tile.h"],
+    "decode": [CSRC + "attn_decode_bf16.hip", CSRC + "attn_fwd_bf16.hip"],
+    "bwd": [CSRC + "attn_bwd_bf16.hip", CSRC + "attn_tile.h"],
+}
 
 
 def counted_flops(B, H, N, d, mask, window=0):
@@ -72,9 +74,9 @@ def _code_only(text):
     return "\n".join(lines)
 
 
-def kernel_source_hash(read=None):
+def kernel_source_hash(kind="fwd", read=None):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kind]:
         if read is None:
             with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
                 text = f.read()
@@ -84,16 +86,16 @@ def kernel_source_hash(read=None):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch from the committed counter runs, only if they were
-    taken on the current kernel sources."""
+def measured_traffic(workload, kind="fwd"):
+    """HBM bytes per step from the committed counter runs, only if they were taken
+    on the current sources of the kernels the workload runs."""
     try:
         with open(TRAFFIC_FILE, encoding="utf-8") as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
     ent = rec.get(workload)
-    if not ent or ent.get("source_hash") != kernel_source_hash():
+    if not ent or ent.get("source_hash") != kernel_source_hash(kind):
         return None
     return ent.get("bytes_per_launch")
 
@@ -253,7 +255,7 @@ def main_decode(args, torch, attn):
                    "wall_s_timed_region": round(wall, 4),
                    "step": "split-range kernel + log-sum-exp merge kernel"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name)},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(name, "decode")},
         "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_kv(wl, q, k, v, args.cpu_budget),
     }
     print(json.dumps(rec), flush=True)
@@ -374,7 +376,7 @@ def main():
 
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
-    traffic = measured_traffic(name if args.which == "fwd" else name + "/bwd")
+    traffic = measured_traffic(name, "fwd") if args.which == "fwd" else measured_traffic(name + "/bwd", "bwd")
     rec = {
         "metric": METRIC if args.which == "fwd" else METRIC_BWD,
         "value": round(tflops, 2),
