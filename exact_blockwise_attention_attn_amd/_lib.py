@@ -26,6 +26,8 @@ ATTN_ERR_BAD_SCALE = -7
 ATTN_ERR_MISALIGNED = -8
 ATTN_ERR_HIP = -9
 ATTN_ERR_WORKSPACE = -10
+ATTN_BLOCK_SPARSE_BLOCK = 128
+ATTN_BLOCK_SPARSE_MAX_BLOCKS = 8192
 
 MASKS = {"none": ATTN_MASK_NONE, "causal": ATTN_MASK_CAUSAL, "window": ATTN_MASK_WINDOW,
          "causal_window": ATTN_MASK_CAUSAL_WINDOW}
@@ -63,6 +65,10 @@ def load():
     lib.attn_fwd_kv_check_args.restype = i
     lib.attn_fwd_kv_workspace_size.argtypes = [i, i, i, i, i]
     lib.attn_fwd_kv_workspace_size.restype = u64
+    lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
+    lib.attn_fwd_block_sparse.restype = i
+    lib.attn_fwd_block_sparse_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i]
+    lib.attn_fwd_block_sparse_check_args.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -109,6 +115,16 @@ def attn_fwd_kv_check_args(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind,
 def attn_fwd_kv_workspace_size(B, H, Nq, Nk, d) -> int:
     """C ``attn_fwd_kv_workspace_size``: workspace bytes ``attn_fwd_kv`` needs."""
     return int(load().attn_fwd_kv_workspace_size(B, H, Nq, Nk, d))
+
+
+def attn_fwd_block_sparse(q, k, v, out, lse, B, H, N, d, scale, causal, layout, dtype, stream):
+    """C ``attn_fwd_block_sparse``: pointers as ints, returns the status code."""
+    return load().attn_fwd_block_sparse(q, k, v, out, lse, B, H, N, d, scale, causal, layout, dtype, stream)
+
+
+def attn_fwd_block_sparse_check_args(q, k, v, out, lse, B, H, N, d, scale, causal, layout, dtype):
+    """C ``attn_fwd_block_sparse_check_args``: host-only argument check, returns the status code."""
+    return load().attn_fwd_block_sparse_check_args(q, k, v, out, lse, B, H, N, d, scale, causal, layout, dtype)
 
 
 def attn_strerror(status: int) -> str:
@@ -237,6 +253,41 @@ def fwd_kv(q, k, v, q_offset=None, mask="none", window=0, scale=None, out=None, 
     with torch.cuda.device(q.device):
         st = attn_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
                          float(scale), mk, int(window), int(q_offset), ATTN_DTYPE_BF16, ws_ptr, ws_bytes, stream)
+    if st != ATTN_OK:
+        raise AttnError(st, attn_strerror(st))
+    return out, lse
+
+
+def fwd_block_sparse(q, k, v, layout, causal=False, scale=None, out=None, lse=None, stream=None):
+    """Block-sparse attention on torch device tensors: q, k, v bf16 [B, H, N, d];
+    ``layout`` a uint8 (or bool) device tensor [H, nb, nb], nb = ceil(N / 128),
+    nonzero = the 128 x 128 block is allowed.  Allocates ``out`` and ``lse`` unless
+    given, enqueues on ``stream`` (default: torch's current stream) and returns
+    (out, lse).  Raises AttnError on any non-zero status."""
+    import torch
+
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must be [B, H, N, d] tensors of one shape")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
+        raise ValueError("the block-sparse forward takes bfloat16 tensors")
+    if not all(t.is_cuda and t.is_contiguous() for t in (q, k, v, layout)):
+        raise ValueError("q, k, v and layout must be contiguous device tensors")
+    B, H, N, d = q.shape
+    nb = -(-N // ATTN_BLOCK_SPARSE_BLOCK)
+    if layout.dtype == torch.bool:
+        layout = layout.to(torch.uint8)
+    if layout.dtype != torch.uint8 or tuple(layout.shape) != (H, nb, nb):
+        raise ValueError(f"layout must be a uint8 tensor [H, {nb}, {nb}]")
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = d ** -0.5
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        st = attn_fwd_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N,
+                                   d, float(scale), 1 if causal else 0, layout.data_ptr(), ATTN_DTYPE_BF16, stream)
     if st != ATTN_OK:
         raise AttnError(st, attn_strerror(st))
     return out, lse

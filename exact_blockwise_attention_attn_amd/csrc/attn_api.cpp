@@ -205,6 +205,42 @@ extern "C" int attn_fwd_kv(const void* q, const void* k, const void* v, void* ou
     return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+extern "C" int attn_fwd_block_sparse_check_args(const void* q, const void* k, const void* v, const void* out,
+                                                const float* lse, int B, int H, int N, int d, float scale, int causal,
+                                                const unsigned char* layout, int dtype) {
+    const int st = attn_check_args(q, k, v, out, lse, B, H, N, d, scale, ATTN_MASK_NONE, 0, dtype);
+    if (st != ATTN_OK) return st;
+    if (!layout) return ATTN_ERR_NULL_PTR;
+    if (causal != 0 && causal != 1) return ATTN_ERR_BAD_MASK;
+    if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_BAD_DTYPE;
+    const uint64_t nb = ((uint64_t)N + ATTN_BLOCK_SPARSE_BLOCK - 1) / ATTN_BLOCK_SPARSE_BLOCK;
+    if (nb > ATTN_BLOCK_SPARSE_MAX_BLOCKS) return ATTN_ERR_BAD_SHAPE;
+    const uint64_t rows = (uint64_t)B * (uint64_t)H * (uint64_t)N;
+    const uint64_t lay = (uint64_t)H * nb * nb;
+    if (overlaps(out, rows * (uint64_t)d * 2, layout, lay) || overlaps(lse, rows * 4, layout, lay))
+        return ATTN_ERR_ALIAS;
+    return ATTN_OK;
+}
+
+extern "C" int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H,
+                                     int N, int d, float scale, int causal, const unsigned char* layout, int dtype,
+                                     void* stream) {
+    const int st = attn_fwd_block_sparse_check_args(q, k, v, out, lse, B, H, N, d, scale, causal, layout, dtype);
+    if (st != ATTN_OK) return st;
+    AttnLaunch a;
+    a.q = q; a.k = k; a.v = v; a.out = out; a.lse = lse;
+    a.B = B; a.H = H; a.N = N; a.d = d;
+    const double c = std::fabs((double)scale) * 1.4426950408889634074;
+    a.c_log2 = (float)(c > 1e-30 ? c : 1e-30);
+    a.negate_q = scale < 0.f ? 1 : 0;
+    a.mask_kind = causal ? ATTN_MASK_CAUSAL : ATTN_MASK_NONE;
+    a.window = 0;
+    a.stream = stream;
+    (void)hipGetLastError();
+    attn_launch_block_bf16(a, layout, causal);
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
 extern "C" const char* attn_strerror(int status) {
     switch (status) {
         case ATTN_OK: return "success";
@@ -223,6 +259,6 @@ extern "C" const char* attn_strerror(int status) {
 }
 
 extern "C" const char* attn_version(void) {
-    return "attn 0.3.0 (gfx950; forward bf16 v_mfma_f32_32x32x16_bf16 and fp32 VALU; split-KV forward bf16; "
-           "backward bf16)";
+    return "attn 0.4.0 (gfx950; forward bf16 v_mfma_f32_32x32x16_bf16 and fp32 VALU; block-sparse forward bf16; "
+           "split-KV forward and decode bf16; backward bf16)";
 }

@@ -144,14 +144,29 @@ struct SplitArgs {
     float* part_lse;   // [BH, n_split, N] fp32 (-inf for a range with no allowed key)
 };
 
-// Two workgroups per CU (two waves per SIMD, <= 256 registers each) where the shape
-// allows it: at 32 rows per wave, d = 128, the unmasked and causal instantiations
-// otherwise take 260 registers and run one wave per SIMD; two waves per SIMD let one
-// wave's softmax overlap the other's matrix instructions (+23% measured on causal
-// cases).  The 64-row shapes need the whole register file; the others already fit.
+// Two workgroups per CU (two waves per SIMD, <= 256 registers each) at 32 rows per
+// wave, d = 128: left alone the compiler takes 260-270 registers for several of these
+// instantiations and runs one wave per SIMD; two waves per SIMD let one wave's
+// softmax overlap the other's matrix instructions (+23% on causal cases, +35% on the
+// narrow window).  The 64-row shapes need the whole register file; at d = 64 the
+// 32-row kernels fit two waves anyway and the cap measured slower.
+// Block-sparse layouts (internal mask kinds of the kernel; the C ABI has its own
+// entry point): the allowed keys of a 128-row query block are the 128-key blocks
+// its layout row marks, intersected with j <= i for the causal variant.
+constexpr int MASK_BLOCK = 16;
+constexpr int MASK_BLOCK_CAUSAL = 17;
+constexpr int BLOCK_TOKENS = 128;      // layout block: one 32-rows-per-wave workgroup, four key tiles
+constexpr int MAX_LAYOUT_BLOCKS = 8192;
+
+struct BlockArgs {
+    const uint8_t* layout;   // [H, nb, nb], nonzero = allowed
+    int H;
+    int nb;                  // ceil(N / BLOCK_TOKENS)
+};
+
 template <int D, int QB, int MASK, bool SPLIT>
 constexpr int min_waves_per_simd() {
-    return (D == 128 && QB == 1 && !SPLIT && (MASK == ATTN_MASK_NONE || MASK == ATTN_MASK_CAUSAL)) ? 2 : 1;
+    return (D == 128 && QB == 1) ? 2 : 1;
 }
 
 template <int D, int QB, int KB, int MASK, bool SPLIT = false>
@@ -159,7 +174,8 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(min_waves_per_simd<D, QB, MASK, SPLIT>(), 8)))
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
-                int BH, int N, int nqt, float c_log2, int negate_q, int window, SplitArgs sa = SplitArgs{}) {
+                int BH, int N, int nqt, float c_log2, int negate_q, int window, SplitArgs sa = SplitArgs{},
+                BlockArgs ba = BlockArgs{}) {
     using C = Cfg<D, QB, KB>;
     constexpr int BC = C::BC;
     constexpr int NS = D / 16;       // 16-dim slabs of the contraction over d
@@ -170,6 +186,11 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     __shared__ __attribute__((aligned(1024))) char kbuf1[C::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char vbuf0[C::TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char vbuf1[C::TILE_BYTES];
+    constexpr bool BLK = (MASK == MASK_BLOCK || MASK == MASK_BLOCK_CAUSAL);
+    constexpr bool CAUS = (MASK == ATTN_MASK_CAUSAL || MASK == MASK_BLOCK_CAUSAL);
+    static_assert(!BLK || (QB == 1 && KB == 1 && !SPLIT), "block layouts use 128-row query blocks of 32-key tiles");
+    __shared__ uint16_t blist[BLK ? MAX_LAYOUT_BLOCKS : 1];   // allowed key blocks of this query block
+    __shared__ int bcount;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -191,7 +212,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         rank = id / BH;
         bh = id - rank * BH;
     }
-    const int qt = (MASK == ATTN_MASK_CAUSAL) ? (nqt - 1 - rank) : rank;
+    const int qt = CAUS ? (nqt - 1 - rank) : rank;
     const int q0 = qt * C::BR;
     // keys: Nk per head, this workgroup's range [kb, ke); query positions offset by qoff
     const int Nk = SPLIT ? sa.Nk : N;
@@ -252,8 +273,38 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             vaddr[r] = ((8 * r + 4 * hl + (s16 >> 2)) * 4 + (k ^ (2 * r + hl))) * 16 + (s16 & 1) * 8;
     }
 
-    int t_lo, t_hi;
-    tile_range<MASK, BC>(q0 + qoff, min(q0 + C::BR, N) - 1 + qoff, Nk, window, t_lo, t_hi);
+    int t_lo = 0, t_hi = -1;
+    if constexpr (BLK) {
+        // this query block's allowed key blocks, in order, compacted by wave 0 (ballots)
+        if (wave == 0) {
+            const uint8_t* lrow = ba.layout + ((size_t)(bh % ba.H) * ba.nb + qt) * ba.nb;
+            const int kmax = CAUS ? min(ba.nb, qt + 1) : ba.nb;   // causal: no key block past the diagonal
+            int cnt = 0;
+            for (int base = 0; base < kmax; base += 64) {
+                const bool on = (base + lane < kmax) && lrow[base + lane] != 0;
+                const unsigned long long m = __ballot(on);
+                if (on) blist[cnt + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)(base + lane);
+                cnt += __popcll(m);
+            }
+            if (lane == 0) bcount = cnt;
+        }
+        __syncthreads();
+        t_hi = 4 * bcount - 1;                  // tiles u = 0 .. 4 count - 1 (t_lo unused)
+        if (t_hi < 0) {
+            // no allowed key for any row of the block: O = 0, LSE = -inf
+            if (my_q[0] < N) {
+                __bf16* Orow = O + (size_t)bh * N * D + (size_t)my_q[0] * D;
+#pragma unroll
+                for (int j = 0; j < D / 32; ++j)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) *reinterpret_cast<bf16x4*>(Orow + j * 32 + 8 * g + 4 * hl) = (bf16x4){};
+                if (hl == 0) LSE[(size_t)bh * N + my_q[0]] = -INFINITY;
+            }
+            return;
+        }
+    } else {
+        tile_range<MASK, BC>(q0 + qoff, min(q0 + C::BR, N) - 1 + qoff, Nk, window, t_lo, t_hi);
+    }
     if constexpr (SPLIT) {
         t_lo = max(t_lo, kb / BC);
         t_hi = min(t_hi, (ke - 1) / BC);
@@ -276,6 +327,12 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         }
     }
     const int n_tiles = t_hi - t_lo + 1;
+    // key tile of step u: the range's u-th tile, or the u-th tile of the allowed blocks
+    // (a block's tiles past the sequence end load the last key row and are masked)
+    auto tile_of = [&](int u) __attribute__((always_inline)) -> int {
+        if constexpr (BLK) return __builtin_amdgcn_readfirstlane(4 * (int)blist[u >> 2] + (u & 3));
+        else return t_lo + u;
+    };
 
     // direct HBM -> LDS load of tile t of one tensor into `dst` (this wave's share)
     auto dma = [&](const __bf16* src, int t, char* dst) __attribute__((always_inline)) {
@@ -287,13 +344,18 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 __builtin_amdgcn_global_load_lds((const void*)(base + ld_off[i]),
                                                  (lds_void*)(dst + (wave * C::LOADS_PER_WAVE + i) * 1024), 16, 0, 0);
         } else {
-            // last tile: rows past the end load the last key row (any valid row; masked later)
-            const int rows_left = Nk - 1 - key0;
+            // last tile: rows past the end load the last key row (any valid row; masked
+            // later).  A tile wholly past the end (the last block of a block layout)
+            // has rows_left < 0 and loads that row for every row.
+            int kb0 = key0;                                                  // first row read
+            if constexpr (BLK) kb0 = min(key0, Nk - 1);     // only block layouts reach past the end
+            const char* tbase = BLK ? reinterpret_cast<const char*>(src + (size_t)kb0 * D) : base;
+            const int rows_left = Nk - 1 - kb0;                              // >= 0
 #pragma unroll
             for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
                 const int row = (int)(ld_off[i] / (2 * D));
                 const uint32_t off = ld_off[i] - (uint32_t)(row - min(row, rows_left)) * (2 * D);
-                __builtin_amdgcn_global_load_lds((const void*)(base + off),
+                __builtin_amdgcn_global_load_lds((const void*)(tbase + off),
                                                  (lds_void*)(dst + (wave * C::LOADS_PER_WAVE + i) * 1024), 16, 0, 0);
             }
         }
@@ -357,7 +419,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int b = 0; b < QB; ++b) {
         const int qi = min(my_q[b], N - 1) + qoff;        // position among the keys
         int lo = 0, hi = Nk - 1;
-        if (MASK == ATTN_MASK_CAUSAL) hi = qi;
+        if (CAUS) hi = qi;
         if (MASK == ATTN_MASK_WINDOW) { lo = max(0, qi - window); hi = min(Nk - 1, qi + window); }
         if (MASK == ATTN_MASK_CAUSAL_WINDOW) { lo = max(0, qi - window); hi = qi; }
         if constexpr (SPLIT) {
@@ -376,7 +438,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         const int key0 = t * BC;
         const int pw0 = qw0 + qoff;                       // position of the wave's first row
         bool need = key0 + BC > Nk;
-        if (MASK == ATTN_MASK_CAUSAL) need |= key0 + BC - 1 > pw0;
+        if (CAUS) need |= key0 + BC - 1 > pw0;
         if (MASK == ATTN_MASK_WINDOW) need |= (key0 < pw0 + C::RW - 1 - window) || (key0 + BC - 1 > pw0 + window);
         if (MASK == ATTN_MASK_CAUSAL_WINDOW) need |= (key0 < pw0 + C::RW - 1 - window) || (key0 + BC - 1 > pw0);
         if constexpr (SPLIT) need |= (key0 < kb) || (key0 + BC > ke);
@@ -545,8 +607,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         for (int k = 0; k < NKS; ++k) { pr[0][b][k] = (bf16x8){}; pr[1][b][k] = (bf16x8){}; }
     for (int i = tid * 16; i < C::TILE_BYTES; i += C::NT * 16)
         *reinterpret_cast<u32x4*>(vbuf1 + i) = (u32x4){0u, 0u, 0u, 0u};
-    dma(Kh, t_lo, kbuf0);
-    if (n_tiles > 1) dma(Kh, t_lo + 1, kbuf1);
+    dma(Kh, BLK ? tile_of(0) : t_lo, kbuf0);
+    if (n_tiles > 1) dma(Kh, BLK ? tile_of(1) : t_lo + 1, kbuf1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     scores(IntC<0>{}, kbuf0);
@@ -556,12 +618,12 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     auto iter = [&](auto parity, int u) __attribute__((always_inline)) {
         constexpr int B = decltype(parity)::value;        // u % 2
         constexpr int X = 1 - B;
-        const int t = t_lo + u;
+        const int t = tile_of(u);
         char* k_own = B ? kbuf1 : kbuf0;                  // held K(t) (consumed); receives K(t+2)
         const char* k_next = B ? kbuf0 : kbuf1;           // K(t+1)
         char* v_own = B ? vbuf1 : vbuf0;                  // held V(t-2) (consumed); receives V(t)
         const char* v_prev = B ? vbuf0 : vbuf1;           // V(t-1)
-        if (u + 2 < n_tiles) dma(Kh, t + 2, k_own);
+        if (u + 2 < n_tiles) dma(Kh, BLK ? tile_of(u + 2) : t + 2, k_own);
         dma(Vh, t, v_own);
         mask_tile(IntC<B>{}, t);
 
@@ -823,6 +885,36 @@ void attn_kv_split_plan(int B, int H, int Nq, int Nk, int* n_split, int* split_l
     len = (len + 31) / 32 * 32;
     *split_len = (int)len;
     *n_split = (int)((Nk + len - 1) / len);
+}
+
+int attn_launch_block_bf16(const AttnLaunch& a, const uint8_t* layout, int causal) {
+    using namespace attn_bf16;
+    BlockArgs ba;
+    ba.layout = layout;
+    ba.H = a.H;
+    ba.nb = (a.N + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
+    const int BH = a.B * a.H;
+    const unsigned grid = (unsigned)((long long)ba.nb * BH);
+    hipStream_t st = (hipStream_t)a.stream;
+    const __bf16 *q = (const __bf16*)a.q, *k = (const __bf16*)a.k, *v = (const __bf16*)a.v;
+    __bf16* o = (__bf16*)a.out;
+    constexpr int NT = Cfg<128, 1, 1>::NT;
+    if (a.d == 128) {
+        if (causal)
+            hipLaunchKernelGGL((fwd_kernel<128, 1, 1, MASK_BLOCK_CAUSAL>), dim3(grid), dim3(NT), 0, st, q, k, v, o, a.lse,
+                               BH, a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba);
+        else
+            hipLaunchKernelGGL((fwd_kernel<128, 1, 1, MASK_BLOCK>), dim3(grid), dim3(NT), 0, st, q, k, v, o, a.lse, BH,
+                               a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba);
+    } else {
+        if (causal)
+            hipLaunchKernelGGL((fwd_kernel<64, 1, 1, MASK_BLOCK_CAUSAL>), dim3(grid), dim3(NT), 0, st, q, k, v, o, a.lse,
+                               BH, a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba);
+        else
+            hipLaunchKernelGGL((fwd_kernel<64, 1, 1, MASK_BLOCK>), dim3(grid), dim3(NT), 0, st, q, k, v, o, a.lse, BH,
+                               a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba);
+    }
+    return 0;
 }
 
 int attn_kv_max_splits(int B, int H, int Nq, int Nk, int d) {

@@ -1,6 +1,8 @@
 // Internal launch descriptor shared by the host entry point and the kernel files.
 #pragma once
 
+#include <stdint.h>
+
 #include "../../include/attn.h"
 
 struct AttnLaunch {
@@ -46,6 +48,9 @@ int attn_launch_f32(const AttnLaunch& a);
 void attn_kv_split_plan(int B, int H, int Nq, int Nk, int* n_split, int* split_len);
 int attn_kv_max_splits(int B, int H, int Nq, int Nk, int d);
 int attn_launch_kv_bf16(const AttnLaunch& a, int Nk, int q_offset, float* part_o, float* part_lse);
+
+// block-sparse forward: layout [H, ceil(N/128), ceil(N/128)] bytes, nonzero = allowed
+int attn_launch_block_bf16(const AttnLaunch& a, const uint8_t* layout, int causal);
 
 // decode (one query per head): the key interval [lo, hi] in ranges, one workgroup each
 int attn_decode_max_splits(int BH, int Nk, int d);

@@ -119,6 +119,33 @@ def make_q_kv(B, H, Nq, Nk, d, dtype=torch.bfloat16, seed=0, q_mult=1.0, device=
     return tuple(out)
 
 
+def random_block_layout(H, nb, density, seed, empty_rows=()):
+    """uint8 [H, nb, nb]: each block allowed with probability ``density`` (seeded);
+    the listed block rows are cleared (query blocks with no allowed key)."""
+    lay = (np.random.default_rng(seed).random((H, nb, nb)) < density).astype(np.uint8)
+    for r in empty_rows:
+        lay[:, r, :] = 0
+    return lay
+
+
+def bigbird_block_layout(H, nb, local=1, n_global=2, n_random=3, seed=0):
+    """uint8 [H, nb, nb] of the sparse-attention pattern the long-sequence pages cite
+    (Longformer / BigBird): a band of ``local`` blocks on each side of the diagonal,
+    ``n_global`` global blocks (the first key blocks for every query block, and every
+    key block for the first query blocks), and ``n_random`` seeded random key blocks
+    per query block, drawn per head."""
+    rng = np.random.default_rng(seed)
+    lay = np.zeros((H, nb, nb), dtype=np.uint8)
+    for h in range(H):
+        for qb in range(nb):
+            lay[h, qb, max(0, qb - local):min(nb, qb + local + 1)] = 1
+            lay[h, qb, :min(n_global, nb)] = 1
+            if n_random:
+                lay[h, qb, rng.choice(nb, size=min(n_random, nb), replace=False)] = 1
+        lay[h, :min(n_global, nb), :] = 1
+    return lay
+
+
 def forced_rows(N, window=0):
     """Rows always checked, so tile and mask boundaries are covered whatever the
     kernel's tile sizes: both ends, power-of-two boundaries and the window edges."""

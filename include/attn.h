@@ -208,6 +208,42 @@ int attn_fwd_kv_check_args(const void* q, const void* k, const void* v, const vo
                            int B, int H, int Nq, int Nk, int d, float scale, int mask_kind, int window,
                            int q_offset, int dtype, const void* workspace, unsigned long long workspace_bytes);
 
+/*
+ * attn_fwd_block_sparse - exact attention restricted to a block layout.
+ *
+ * The keys are cut into blocks of ATTN_BLOCK_SPARSE_BLOCK (128) tokens and so are
+ * the queries; layout[h][qb][kb] != 0 allows every key of block kb for every query
+ * of block qb in head h (the same layout for every batch entry).  With causal = 1
+ * the layout is intersected with j <= i.  For every allowed set A(i) the result is
+ * exact attention over A(i), as attn_fwd computes it for its masks; a row with no
+ * allowed key gets O = 0 and LSE = -inf.  Blocks the layout excludes are never
+ * read: the block-sparse attention that the long-sequence inference page
+ * ("长序列推理中的注意力机制优化策略与实践", §2.1 sparse attention, §7 block-sparse as
+ * the configuration for AMD parts) and the Mosaic long-sequence attention page
+ * (§6, block sparsity beyond 100K tokens) describe, as a whole-tile skip.
+ *
+ *   q, k, v, out, lse, B, H, N, d, scale  as for attn_fwd (bf16 only).
+ *   causal    0 or 1.
+ *   layout    device pointer to H x nb x nb bytes, nb = ceil(N / 128), row-major
+ *             [H, nb, nb]; read only.  nb <= ATTN_BLOCK_SPARSE_MAX_BLOCKS.
+ *   dtype     ATTN_DTYPE_BF16 (ATTN_DTYPE_F32: ATTN_ERR_BAD_DTYPE).
+ *   stream    a hipStream_t (NULL = the default stream) on the current device.
+ *
+ * Ownership and errors as for attn_fwd; out or lse overlapping the layout is
+ * ATTN_ERR_ALIAS, a missing layout ATTN_ERR_NULL_PTR, causal outside {0, 1}
+ * ATTN_ERR_BAD_MASK.
+ */
+enum { ATTN_BLOCK_SPARSE_BLOCK = 128, ATTN_BLOCK_SPARSE_MAX_BLOCKS = 8192 };
+
+int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int B, int H, int N, int d, float scale, int causal,
+                          const unsigned char* layout, int dtype, void* stream);
+
+/* attn_fwd_block_sparse_check_args - its host-side argument check, on its own. */
+int attn_fwd_block_sparse_check_args(const void* q, const void* k, const void* v, const void* out,
+                                     const float* lse, int B, int H, int N, int d, float scale, int causal,
+                                     const unsigned char* layout, int dtype);
+
 /* attn_strerror - static, NUL-terminated text for a status code (never NULL). */
 const char* attn_strerror(int status);
 

@@ -22,8 +22,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_check_args", "attn_check_args", "attn_fwd",
-                                    "attn_fwd_kv", "attn_fwd_kv_check_args", "attn_fwd_kv_workspace_size",
-                                    "attn_strerror", "attn_version"]
+                                    "attn_fwd_block_sparse", "attn_fwd_block_sparse_check_args", "attn_fwd_kv",
+                                    "attn_fwd_kv_check_args", "attn_fwd_kv_workspace_size", "attn_strerror",
+                                    "attn_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -238,3 +239,40 @@ def test_kv_rejects_before_any_launch():
     assert st == _lib.ATTN_ERR_BAD_SHAPE
     st = attn.attn_fwd_kv(q, k, v, o, l, 1, 8, 1, 65536, 128, 0.1, 0, 0, 0, 1, 0, 0, None)
     assert st == _lib.ATTN_ERR_WORKSPACE
+
+
+# ---- block-sparse forward: host checks
+def bscheck(**kw):
+    q, k, v, o, l, lay = [BASE + i * GAP for i in range(6)]
+    a = dict(q=q, k=k, v=v, out=o, lse=l, B=2, H=4, N=1000, d=128, scale=0.1, causal=0, layout=lay, dtype=1)
+    a.update(kw)
+    return attn.attn_fwd_block_sparse_check_args(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["N"],
+                                                 a["d"], a["scale"], a["causal"], a["layout"], a["dtype"])
+
+
+def test_block_sparse_valid_arguments_pass():
+    assert bscheck() == _lib.ATTN_OK
+    assert bscheck(causal=1, d=64, scale=-0.5) == _lib.ATTN_OK
+    assert bscheck(N=128 * 8192, B=1, H=1, d=64) == _lib.ATTN_OK          # the largest layout
+    assert bscheck(layout=BASE + 5 * GAP + 1) == _lib.ATTN_OK               # bytes: no alignment needed
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(layout=0), _lib.ATTN_ERR_NULL_PTR), (dict(q=0), _lib.ATTN_ERR_NULL_PTR),
+    (dict(causal=2), _lib.ATTN_ERR_BAD_MASK), (dict(causal=-1), _lib.ATTN_ERR_BAD_MASK),
+    (dict(dtype=0), _lib.ATTN_ERR_BAD_DTYPE),
+    (dict(N=128 * 8192 + 1, B=1, H=1, d=64), _lib.ATTN_ERR_BAD_SHAPE),     # more than 8192 layout blocks
+    (dict(N=0), _lib.ATTN_ERR_BAD_SHAPE), (dict(d=96), _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM),
+    (dict(layout=BASE + 3 * GAP + 100), _lib.ATTN_ERR_ALIAS),             # layout inside out
+    (dict(layout=BASE + 4 * GAP + 8), _lib.ATTN_ERR_ALIAS),               # layout inside lse
+    (dict(out=BASE), _lib.ATTN_ERR_ALIAS),
+])
+def test_block_sparse_invalid_arguments(kw, code):
+    assert bscheck(**kw) == code
+
+
+def test_block_sparse_rejects_before_any_launch():
+    q, k, v, o, l, lay = [BASE + i * GAP for i in range(6)]
+    assert attn.attn_fwd_block_sparse(q, k, v, o, l, 1, 1, 100, 96, 0.1, 0, lay, 1, None) == \
+        _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM
+    assert attn.attn_fwd_block_sparse(q, k, v, o, l, 1, 1, 100, 64, 0.1, 0, 0, 1, None) == _lib.ATTN_ERR_NULL_PTR

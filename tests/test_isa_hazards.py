@@ -82,8 +82,9 @@ def test_bf16_kernel_asm_mfma_sources_not_written_by_valu():
         assert res.returncode == 0, res.stderr
         text = open(out, encoding="utf-8").read()
     names = re.findall(r"^(_ZN9attn_bf1610fwd_kernel\w+):", text, re.M)
-    # d in {64, 128} x 4 masks x (rows per wave {32, 64}, plus the split-KV mode at 32)
-    assert len(names) == 24
+    # d in {64, 128} x (4 masks x (rows per wave {32, 64}, plus the split-KV mode at 32)
+    # + the two block-layout kinds at 32 rows per wave)
+    assert len(names) == 28
     for name in names:
         body = text[text.index(name + ":"):]
         body = body[:body.index(".Lfunc_end")]      # the whole function (early exits included)
