@@ -7,7 +7,7 @@ Prints one JSON line: TFLOP/s of counted FLOPs (4 B H N^2 d dense, halved for
 causal, band pairs for the window), the roofline position of the kernel and the
 CPU oracle timed on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--pass fwd|bwd|decode]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--pass fwd|bwd|decode|sparse]
 
 --pass bwd times the backward (attn_bwd: dq, dk, dv from dout, O and LSE) on the
 same workload instead, counted as 2.5x the forward's FLOPs (the five products of
@@ -17,6 +17,9 @@ the backward: the recomputed scores, dP, dV, dK and dQ).
 against a key/value cache; default B=1 H=32 Nk=131072 d=128 causal).  That work is
 bound by HBM bandwidth, so the figure is GB/s of the bytes the step must move (the
 K and V cache read once, q read, O and LSE written) against the 8 TB/s peak.
+
+--pass sparse times attn_fwd_block_sparse on a BigBird-style block layout (default
+B=1 H=32 N=32768 d=128): TFLOP/s counted on the allowed (query, key) pairs only.
 """
 from __future__ import annotations
 
@@ -35,6 +38,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, d=128 N=8192 causal"
 METRIC_BWD = "attention bwd TFLOP/s (2.5x forward FLOPs) and % of bf16 MFMA peak"
 METRIC_DECODE = "attention decode (split-KV) GB/s of K/V cache read and % of HBM peak"
+METRIC_SPARSE = "block-sparse attention fwd TFLOP/s on allowed pairs and % of bf16 MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense bf16 MFMA; fp32 vector
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -261,13 +265,121 @@ def main_decode(args, torch, attn):
     print(json.dumps(rec), flush=True)
 
 
+def layout_pairs(layout, N, block, causal):
+    """Allowed (query, key) pairs of a block layout [H, nb, nb] (summed over heads)."""
+    nb = layout.shape[1]
+    sizes = np.minimum(block, N - block * np.arange(nb))           # tokens per block (last one ragged)
+    total = 0
+    for h in range(layout.shape[0]):
+        lay = layout[h] != 0
+        if not causal:
+            total += int(sizes @ lay.astype(np.int64) @ sizes)
+        else:
+            for qb in range(nb):
+                for kb in np.nonzero(lay[qb, :qb + 1])[0]:
+                    if kb < qb:
+                        total += int(sizes[qb] * sizes[kb])
+                    else:                                       # diagonal block: j <= i
+                        total += int(sizes[qb] * (sizes[qb] + 1) // 2)
+    return total
+
+
+def cpu_baseline_sparse(wl, layout, q, k, v, budget_s=20.0):
+    """The block-sparse oracle, untuned, on whole heads x 1024 seeded query rows
+    until about ``budget_s`` of CPU time, in the line's unit (allowed-pair flops)."""
+    from oracle.attention_block_ref import attention_forward_block_sparse, block_allowed
+    from exact_blockwise_attention_attn_amd.inputs import sample_rows
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    rows = sample_rows(wl.N, 1024, seed=12345)
+    BH = wl.B * wl.H
+    heads, elapsed, flops = 0, 0.0, 0
+    while heads < BH and elapsed < budget_s:
+        b, h = divmod(heads, wl.H)
+        args = [x[b:b + 1, h:h + 1].float().cpu().numpy() for x in (q, k, v)]
+        ts = time.perf_counter()
+        attention_forward_block_sparse(*args, wl.softmax_scale, layout[h:h + 1], 128, wl.causal, rows=rows)
+        elapsed += time.perf_counter() - ts
+        flops += 4 * wl.d * int(block_allowed(layout[h], rows, wl.N, 128, wl.causal).sum())
+        heads += 1
+    full = 4 * wl.d * layout_pairs(layout, wl.N, 128, wl.causal) * wl.B
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "extrapolated_full_workload_s": round(elapsed * full / flops, 1),
+            "sample": f"{heads} of {BH} (b,h) heads x {len(rows)} seeded query rows each (N={wl.N}, d={wl.d}, "
+                      f"BigBird layout), numpy float64, {elapsed:.1f} s",
+            "seconds": elapsed}
+
+
+def main_sparse(args, torch, attn):
+    from exact_blockwise_attention_attn_amd.inputs import SPARSE_HEADLINE, SPARSE_WORKLOADS, make_qkv
+
+    name = args.workload or SPARSE_HEADLINE
+    wl = SPARSE_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v = make_qkv(wl.B, wl.H, wl.N, wl.d, torch.bfloat16, seed=args.seed, device="cuda")
+    layout = wl.layout(seed=args.seed)
+    lay_d = torch.from_numpy(layout).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+
+    def step():
+        attn.fwd_block_sparse(q, k, v, lay_d, causal=wl.causal, scale=wl.softmax_scale, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    assert torch.isfinite(out).all(), "non-finite output"
+    pairs = layout_pairs(layout, wl.N, 128, wl.causal) * wl.B
+    flops = 4 * wl.d * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    rec = {
+        "metric": METRIC_SPARSE,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) q, k, v drawn on the device; seeded BigBird-style block layout",
+        "config": {"workload": name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d, "block": 128, "local": wl.local,
+                   "global": wl.n_global, "random": wl.n_random, "causal": wl.causal,
+                   "layout_density": round(float(layout.mean()), 4), "allowed_pairs": pairs, "flops_per_step": flops,
+                   "pct_of_peak": round(100.0 * tflops / peak, 2),
+                   "ms_median": round(per_step[len(per_step) // 2], 5), "ms_min": round(per_step[0], 5),
+                   "wall_s_timed_region": round(wall, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": measured_traffic(name, "fwd")},
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_sparse(wl, layout, q, k, v, args.cpu_budget),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "decode"], default="fwd")
+    ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "decode", "sparse"], default="fwd")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
@@ -296,6 +408,9 @@ def main():
     attn.load()
     if args.which == "decode":
         main_decode(args, torch, attn)
+        return
+    if args.which == "sparse":
+        main_sparse(args, torch, attn)
         return
     name = args.workload or HEADLINE
     wl = WORKLOADS[name]

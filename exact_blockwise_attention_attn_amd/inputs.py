@@ -119,6 +119,35 @@ def make_q_kv(B, H, Nq, Nk, d, dtype=torch.bfloat16, seed=0, q_mult=1.0, device=
     return tuple(out)
 
 
+@dataclass(frozen=True)
+class SparseWorkload:
+    """A block-sparse workload: BigBird-style layout (local band, global and random
+    blocks, see ``bigbird_block_layout``) over 128-token blocks, bf16."""
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    local: int
+    n_global: int
+    n_random: int
+    causal: bool = False
+
+    @property
+    def softmax_scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.d)))
+
+    def layout(self, seed=0):
+        return bigbird_block_layout(self.H, -(-self.N // 128), self.local, self.n_global, self.n_random, seed)
+
+
+SPARSE_WORKLOADS = {
+    "bigbird_bf16_h32_n32768_d128": SparseWorkload("bigbird_bf16_h32_n32768_d128", 1, 32, 32768, 128, 1, 2, 3),
+}
+
+SPARSE_HEADLINE = "bigbird_bf16_h32_n32768_d128"
+
+
 def random_block_layout(H, nb, density, seed, empty_rows=()):
     """uint8 [H, nb, nb]: each block allowed with probability ``density`` (seeded);
     the listed block rows are cleared (query blocks with no allowed key)."""
