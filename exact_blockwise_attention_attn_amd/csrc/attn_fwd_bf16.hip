@@ -371,11 +371,14 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     float m_run[QB], l_exp[QB], l_rnd[QB];     // running max (log2 domain, lazily raised), sum p, sum bf16(p)
 #pragma unroll
     for (int b = 0; b < QB; ++b) { m_run[b] = -INFINITY; l_exp[b] = 0.f; l_rnd[b] = 0.f; }
-    // At d = 64 the vector ALUs, not the matrix cores, bound a tile, so the sum of
-    // the bf16-rounded probabilities moves to the matrix cores: a product with an
-    // all-ones A operand puts each query's sum over a 16-key slab in every row of its
-    // column, so each register of a lane accumulates the full row sum (both halves).
-    constexpr bool RSM = (D == 64);
+    // The sum of the bf16-rounded probabilities can run on the matrix cores: a
+    // product with an all-ones A operand puts each query's sum over a 16-key slab in
+    // every row of its column, so each register of a lane accumulates the full row
+    // sum (both halves).  It trades 2 vector instructions per score for one matrix
+    // instruction per slab: a gain where the vector ALUs bound the tile (d = 64;
+    // d = 128 at 64 rows per wave, +1-3% on the causal 8192-token case), a loss at 32
+    // rows per wave and d = 128, whose two-waves-per-SIMD register cap it overflows.
+    constexpr bool RSM = (D == 64) || (QB == 2);
     f32x16 lr_acc[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b)
