@@ -9,9 +9,13 @@
 //
 // A workgroup owns 64 query rows; each row is owned by D/64 neighbouring lanes
 // holding 64 of its dimensions, whose partial dot products are combined with a
-// lane shuffle.  K/V tiles of 32 keys are staged in LDS (lanes of one half read the
-// same key row: an LDS broadcast) and each row keeps a running maximum and sum,
-// normalising once at the end ("Blockwise Parallel Transformer in PyTorch", the
+// lane shuffle.  The 256 threads form KS = 256 / (64 D/64) groups of such lanes,
+// and group g takes every KS-th key tile of the workgroup's range, so the serial
+// chain of a row is 1/KS of its keys.  K/V tiles of 32 keys are staged in LDS, one
+// pair per group (lanes of one half read the same key row: an LDS broadcast), and
+// each group keeps a running maximum and sum per row.  At the end the groups'
+// partial results are combined exactly (each rescaled to the common maximum) and
+// normalised once ("Blockwise Parallel Transformer in PyTorch", the
 // blockwise_attention example and its numerical-stability pitfall; Mosaic
 // long-sequence attention page, §3.2 and §5.1).
 
@@ -35,19 +39,28 @@ __device__ __forceinline__ bool key_allowed(int qi, int kj, int N, int window) {
     return true;
 }
 
+constexpr int NTHREADS = 256;
+
 template <int D, int MASK>
-__global__ __launch_bounds__(ROWS * (D / DD))
+__global__ __launch_bounds__(NTHREADS)
 void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                 float* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqt,
                 float c_log2, int negate_q, int window) {
     constexpr int SPLIT = D / DD;             // lanes per row
-    constexpr int NT = ROWS * SPLIT;
-    __shared__ __attribute__((aligned(16))) float Ks[TK * D];
-    __shared__ __attribute__((aligned(16))) float Vs[TK * D];
+    constexpr int GT = ROWS * SPLIT;          // threads of one key group
+    constexpr int KS = NTHREADS / GT;         // key groups
+    constexpr int TILE = TK * D;              // floats of one K or V tile
+    // per group a K and a V tile; reused at the end for the groups' partial results
+    __shared__ __attribute__((aligned(16))) float smem[2 * KS * TILE];
+    static_assert((KS - 1) * GT * (DD + 4) <= 2 * KS * TILE, "merge area fits the tile buffers");
 
     const int tid = threadIdx.x;
-    const int part = tid % SPLIT;             // which 64 dimensions
-    const int row = tid / SPLIT;
+    const int grp = tid / GT;                 // which key group
+    const int lt = tid - grp * GT;
+    const int part = lt % SPLIT;              // which 64 dimensions
+    const int row = lt / SPLIT;
+    float* Ks = smem + grp * 2 * TILE;
+    float* Vs = Ks + TILE;
     const int id = blockIdx.x;
     const int rank = id / BH;
     const int bh = id - rank * BH;
@@ -77,49 +90,87 @@ void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const 
     if (MASK == ATTN_MASK_CAUSAL_WINDOW) { lo = max(0, q0 - window) / TK; hi = min(last, r1 / TK); }
     const double c = (double)c_log2;
 
-    for (int t = lo; t <= hi; ++t) {
+    // rounds: group g takes tile t0 + g; every group passes the same barriers
+    for (int t0 = lo; t0 <= hi; t0 += KS) {
+        const int t = t0 + grp;
+        const bool mine = t <= hi;
         const int key0 = t * TK;
-        for (int e = tid * 4; e < TK * D; e += NT * 4) {
-            const int kr = e / D, col = e % D;
-            float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-            if (key0 + kr < N) {
-                kv = *reinterpret_cast<const float4*>(K + head + (size_t)(key0 + kr) * D + col);
-                vv = *reinterpret_cast<const float4*>(V + head + (size_t)(key0 + kr) * D + col);
+        if (mine) {
+            for (int e = lt * 4; e < TILE; e += GT * 4) {
+                const int kr = e / D, col = e % D;
+                float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+                if (key0 + kr < N) {
+                    kv = *reinterpret_cast<const float4*>(K + head + (size_t)(key0 + kr) * D + col);
+                    vv = *reinterpret_cast<const float4*>(V + head + (size_t)(key0 + kr) * D + col);
+                }
+                *reinterpret_cast<float4*>(Ks + e) = kv;
+                *reinterpret_cast<float4*>(Vs + e) = vv;
             }
-            *reinterpret_cast<float4*>(Ks + e) = kv;
-            *reinterpret_cast<float4*>(Vs + e) = vv;
         }
         __syncthreads();
-
-        double s[TK];
-        double mt = -INFINITY;
+        if (mine) {
+            double s[TK];
+            double mt = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < TK; ++j) {
-            double dot = 0.0;
+            for (int j = 0; j < TK; ++j) {
+                double dot = 0.0;
 #pragma unroll
-            for (int cc = 0; cc < DD; ++cc) dot = __builtin_fma((double)q[cc], (double)Ks[j * D + dof + cc], dot);
-            if (SPLIT == 2) dot += __shfl_xor(dot, 1);
-            s[j] = key_allowed<MASK>(my_q, key0 + j, N, window) ? dot * c : -INFINITY;
-            mt = fmax(mt, s[j]);
+                for (int cc = 0; cc < DD; ++cc) dot = __builtin_fma((double)q[cc], (double)Ks[j * D + dof + cc], dot);
+                if (SPLIT == 2) dot += __shfl_xor(dot, 1);
+                s[j] = key_allowed<MASK>(my_q, key0 + j, N, window) ? dot * c : -INFINITY;
+                mt = fmax(mt, s[j]);
+            }
+            const double m_new = fmax(m, mt);
+            const double base = (m_new == -INFINITY) ? 0.0 : m_new;
+            const float alpha = __builtin_amdgcn_exp2f((float)(m - base));
+            l *= alpha;
+#pragma unroll
+            for (int cc = 0; cc < DD; ++cc) acc[cc] *= alpha;
+#pragma unroll
+            for (int j = 0; j < TK; ++j) {
+                const float p = __builtin_amdgcn_exp2f((float)(s[j] - base));
+                l += p;
+#pragma unroll
+                for (int cc = 0; cc < DD; ++cc) acc[cc] = __builtin_fmaf(p, Vs[j * D + dof + cc], acc[cc]);
+            }
+            m = m_new;
         }
-        const double m_new = fmax(m, mt);
-        const double base = (m_new == -INFINITY) ? 0.0 : m_new;
-        const float alpha = __builtin_amdgcn_exp2f((float)(m - base));
-        l *= alpha;
-#pragma unroll
-        for (int cc = 0; cc < DD; ++cc) acc[cc] *= alpha;
-#pragma unroll
-        for (int j = 0; j < TK; ++j) {
-            const float p = __builtin_amdgcn_exp2f((float)(s[j] - base));
-            l += p;
-#pragma unroll
-            for (int cc = 0; cc < DD; ++cc) acc[cc] = __builtin_fmaf(p, Vs[j * D + dof + cc], acc[cc]);
-        }
-        m = m_new;
         __syncthreads();
     }
 
-    if (my_q < N) {
+    // combine the groups: groups 1.. park (acc, l, m) in LDS, group 0 rescales and sums
+    if (KS > 1) {
+        float* slot = smem + ((grp - 1) * GT + lt) * (DD + 4);
+        if (grp > 0) {
+#pragma unroll
+            for (int cc = 0; cc < DD; cc += 4)
+                *reinterpret_cast<float4*>(slot + cc) = make_float4(acc[cc], acc[cc + 1], acc[cc + 2], acc[cc + 3]);
+            slot[DD] = l;
+            *reinterpret_cast<double*>(slot + DD + 2) = m;
+        }
+        __syncthreads();
+        if (grp == 0) {
+            double M = m;
+#pragma unroll
+            for (int g = 1; g < KS; ++g) M = fmax(M, *reinterpret_cast<const double*>(smem + ((g - 1) * GT + lt) * (DD + 4) + DD + 2));
+            const float w0 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((float)(m - M));
+            l *= w0;
+#pragma unroll
+            for (int cc = 0; cc < DD; ++cc) acc[cc] *= w0;
+#pragma unroll
+            for (int g = 1; g < KS; ++g) {
+                const float* sg = smem + ((g - 1) * GT + lt) * (DD + 4);
+                const double mg = *reinterpret_cast<const double*>(sg + DD + 2);
+                const float wg = (mg == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((float)(mg - M));
+                l = __builtin_fmaf(wg, sg[DD], l);
+#pragma unroll
+                for (int cc = 0; cc < DD; ++cc) acc[cc] = __builtin_fmaf(wg, sg[cc], acc[cc]);
+            }
+            m = M;
+        }
+    }
+
+    if (grp == 0 && my_q < N) {
         const float inv = 1.0f / l;
 #pragma unroll
         for (int cc = 0; cc < DD; cc += 4) {
@@ -136,7 +187,7 @@ template <int D, int MASK>
 static int launch(const AttnLaunch& a) {
     const int nqt = (a.N + ROWS - 1) / ROWS;
     const long long grid = (long long)nqt * a.B * a.H;
-    hipLaunchKernelGGL((fwd_kernel<D, MASK>), dim3((unsigned)grid), dim3(ROWS * (D / DD)), 0,
+    hipLaunchKernelGGL((fwd_kernel<D, MASK>), dim3((unsigned)grid), dim3(NTHREADS), 0,
                        (hipStream_t)a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
                        (float*)a.out, a.lse, a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window);
     return 0;
