@@ -241,12 +241,6 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             if (negate_q) raw ^= 0x80008000u;    // exact sign flip: scale < 0 runs as -q with |scale|
             qreg[b][s] = __builtin_bit_cast(bf16x8, raw);
         }
-    // the operands sit in AGPRs from here on, written (and padded) well before any MFMA reads them
-#pragma unroll
-    for (int b = 0; b < QB; ++b)
-#pragma unroll
-        for (int s = 0; s < NS; ++s) settle_qa(qreg[b][s]);
-
     // ---- per-lane LDS and load addresses (byte offsets within a tile)
     // loader: wave instruction i fills 1 KB block b = wave * LPW + i, i.e. rows
     // 16 (b % RB) .. +15 of chunk group b / RB; lane -> (row, chunk)
@@ -280,11 +274,18 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             const uint8_t* lrow = ba.layout + ((size_t)(bh % ba.H) * ba.nb + qt) * ba.nb;
             const int kmax = CAUS ? min(ba.nb, qt + 1) : ba.nb;   // causal: no key block past the diagonal
             int cnt = 0;
-            for (int base = 0; base < kmax; base += 64) {
-                const bool on = (base + lane < kmax) && lrow[base + lane] != 0;
-                const unsigned long long m = __ballot(on);
-                if (on) blist[cnt + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)(base + lane);
-                cnt += __popcll(m);
+            for (int base = 0; base < kmax; base += 256) {
+                uint8_t byte[4];                 // four loads in flight per lane (clamped, then tested)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) byte[k] = lrow[min(base + 64 * k + lane, kmax - 1)];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int blk = base + 64 * k + lane;
+                    const bool on = blk < kmax && byte[k] != 0;
+                    const unsigned long long m = __ballot(on);
+                    if (on) blist[cnt + __popcll(m & ((1ull << lane) - 1ull))] = (uint16_t)blk;
+                    cnt += __popcll(m);
+                }
             }
             if (lane == 0) bcount = cnt;
         }
@@ -612,7 +613,15 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         *reinterpret_cast<u32x4*>(vbuf1 + i) = (u32x4){0u, 0u, 0u, 0u};
     dma(Kh, BLK ? tile_of(0) : t_lo, kbuf0);
     if (n_tiles > 1) dma(Kh, BLK ? tile_of(1) : t_lo + 1, kbuf1);
+    // Q was requested at kernel start and is waited for only here (the wait orders
+    // the pinning below after the tile requests), so the Q loads and the first K
+    // tiles are in flight together.  From here on Q sits in AGPRs, written (and
+    // padded) well before any MFMA reads it.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) settle_qa(qreg[b][s]);
     __syncthreads();
     scores(IntC<0>{}, kbuf0);
     settle_scores(IntC<0>{});
@@ -696,6 +705,16 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     if (u & 1) pv(IntC<0>{}, vbuf0); else pv(IntC<1>{}, vbuf1);
 
     // ---- epilogue: O = acc / sum bf16(p) (bf16, nearest even), LSE = (m + log2 sum p) ln 2
+    // A lane holds 16 values of one O row, so direct stores would write 16-byte
+    // pieces of 32 rows per instruction.  Instead each wave stages a 32-row block in
+    // one of the (now idle) tile buffers, row-major with the 16-byte chunks rotated
+    // by the row (no bank conflicts), and writes whole rows: 1 KB per instruction.
+    const bool partials = SPLIT && sa.n_split > 1;
+    if (!partials) __syncthreads();      // every wave is done with the tile buffers
+    char* const stage = wave == 0 ? kbuf0 : wave == 1 ? kbuf1 : wave == 2 ? vbuf0 : vbuf1;
+    constexpr int ROWB = 2 * D;          // bytes of one bf16 O row
+    constexpr int NCH = D / 8;           // 16-byte chunks per row
+    static_assert(32 * ROWB <= C::TILE_BYTES, "a 32-row block of O fits one tile buffer");
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
         const float le = swap32_add(l_exp[b]);
@@ -720,22 +739,33 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             }
             continue;
         }
-        if (my_q[b] < N) {
-            const float inv = 1.0f / lr;
-            __bf16* Orow = O + head + (size_t)my_q[b] * D;
+        // stage: row ln, elements j 32 + 8 g + 4 hl .. +3 = half hl of chunk 4 j + g
+        // (rows past the sequence end are staged too, never stored)
+        const float inv = 1.0f / lr;
 #pragma unroll
-            for (int j = 0; j < ND; ++j) {
+        for (int j = 0; j < ND; ++j) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    bf16x4 val;
+            for (int g = 0; g < 4; ++g) {
+                bf16x4 val;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[b][j][4 * g + e] * inv);
-                    *reinterpret_cast<bf16x4*>(Orow + j * 32 + 8 * g + 4 * hl) = val;
-                }
+                for (int e = 0; e < 4; ++e) val[e] = (__bf16)(o[b][j][4 * g + e] * inv);
+                const int c = 4 * j + g;
+                *reinterpret_cast<bf16x4*>(stage + ln * ROWB + ((c ^ (ln & (NCH - 1))) * 16) + 8 * hl) = val;
             }
-            if (hl == 0)
-                LSE[(size_t)bh * N + my_q[b]] = (m_run[b] + __builtin_amdgcn_logf(le)) * 0.69314718055994531f;
         }
+        __builtin_amdgcn_wave_barrier();     // the wave's LDS writes precede its reads (in order per wave)
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < 32 * ROWB / 1024; ++i) {
+            const int f = i * 1024 + lane * 16;
+            const int row = f / ROWB, c = (f % ROWB) / 16;
+            const u32x4 val = *reinterpret_cast<const u32x4*>(stage + row * ROWB + ((c ^ (row & (NCH - 1))) * 16));
+            const int qrow = qw0 + 32 * b + row;
+            if (qrow < N) *reinterpret_cast<u32x4*>(O + head + (size_t)qrow * D + c * 8) = val;
+        }
+        asm volatile("" ::: "memory");       // the next block's staging writes follow these reads
+        if (hl == 0 && my_q[b] < N)
+            LSE[(size_t)bh * N + my_q[b]] = (m_run[b] + __builtin_amdgcn_logf(le)) * 0.69314718055994531f;
     }
 }
 
