@@ -175,7 +175,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
                 int BH, int N, int nqt, float c_log2, int negate_q, int window, SplitArgs sa = SplitArgs{},
-                BlockArgs ba = BlockArgs{}) {
+                BlockArgs ba = BlockArgs{}, int hg = 0) {
     using C = Cfg<D, QB, KB>;
     constexpr int BC = C::BC;
     constexpr int NS = D / 16;       // 16-dim slabs of the contraction over d
@@ -198,9 +198,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int hl = lane >> 5;        // lane half
     const int ln = lane & 31;
 
-    // Heaviest query blocks first for the causal mask; the (batch, head) index
-    // varies fastest, so with BH a multiple of 8 every block of a head lands on the
-    // same XCD (workgroups are dealt to the 8 XCDs round robin) and shares its L2.
+    // Workgroup order: heads in groups of hg (grouped_order), inside a group the
+    // heaviest query blocks first for the causal mask.
     const int id = blockIdx.x;
     int rank, bh, split = 0;
     if constexpr (SPLIT) {
@@ -209,8 +208,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         split = rem / BH;
         bh = rem - split * BH;
     } else {
-        rank = id / BH;
-        bh = id - rank * BH;
+        grouped_order(id, BH, nqt, hg, rank, bh);
     }
     const int qt = CAUS ? (nqt - 1 - rank) : rank;
     const int q0 = qt * C::BR;
@@ -776,7 +774,8 @@ static int launch(const AttnLaunch& a) {
     const long long grid = (long long)nqt * a.B * a.H;
     hipLaunchKernelGGL((fwd_kernel<D, QB, KB, MASK>), dim3((unsigned)grid), dim3(C::NT), 0, (hipStream_t)a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.out, a.lse,
-                       a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window);
+                       a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window, SplitArgs{}, BlockArgs{},
+                       head_group(a.N, a.d));   // K and V of a head: causal B4 H32 N16384 d128 +15%
     return 0;
 }
 

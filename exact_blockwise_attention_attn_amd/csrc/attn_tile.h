@@ -21,6 +21,31 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 template <int V>
 struct IntC { static constexpr int value = V; };
 
+// Workgroup order over (block rank, head) pairs: the BH (batch, head) pairs in
+// groups of hg (all of them when hg is 0), every rank of a group before the next
+// group, the head varying fastest inside a group.  With hg a multiple of 8 every
+// block of a head lands on the same XCD (workgroups are dealt to the 8 XCDs round
+// robin) and shares its L2, and a group's K and V (or Q and dO) stay resident in
+// the Infinity Cache while the group runs.
+__device__ __forceinline__ void grouped_order(int id, int BH, int n_rank, int hg, int& rank, int& bh) {
+    const int G = (hg > 0 && hg < BH) ? hg : BH;    // heads per group
+    const int full = BH / G;                         // full groups; a last one holds BH - full G
+    const int g = id / (G * n_rank);
+    const int gsz = g < full ? G : BH - full * G;
+    const int r = id - g * (G * n_rank);
+    rank = r / gsz;
+    bh = g * G + (r - rank * gsz);
+}
+
+// Heads per group for a kernel that streams two [N, d] bf16 tensors of a head: the
+// largest multiple of 8 whose two tensors fit in 128 MB (half the 256 MB Infinity
+// Cache), at least 8 (one head per XCD).
+inline int head_group(int N, int d) {
+    const long long per_head = 2LL * N * d * 2;
+    const long long fit = (128LL << 20) / (8 * per_head);
+    return 8 * (int)(fit < 1 ? 1 : (fit > (1 << 20) ? (1 << 20) : fit));
+}
+
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
     if constexpr (I < N) {
