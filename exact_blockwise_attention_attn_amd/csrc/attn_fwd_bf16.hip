@@ -772,10 +772,11 @@ static int launch(const AttnLaunch& a) {
     using C = Cfg<D, QB, KB>;
     const int nqt = (a.N + C::BR - 1) / C::BR;
     const long long grid = (long long)nqt * a.B * a.H;
+    int hg = head_group_override();
+    if (hg < 0) hg = head_group(a.N, a.d);      // K and V of a head: causal B4 H32 N16384 d128 +12%
     hipLaunchKernelGGL((fwd_kernel<D, QB, KB, MASK>), dim3((unsigned)grid), dim3(C::NT), 0, (hipStream_t)a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.out, a.lse,
-                       a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window, SplitArgs{}, BlockArgs{},
-                       head_group(a.N, a.d));   // K and V of a head: causal B4 H32 N16384 d128 +15%
+                       a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window, SplitArgs{}, BlockArgs{}, hg);
     return 0;
 }
 
