@@ -156,6 +156,7 @@ struct SplitArgs {
 constexpr int MASK_BLOCK = 16;
 constexpr int MASK_BLOCK_CAUSAL = 17;
 constexpr int BLOCK_TOKENS = 128;      // layout block: one 32-rows-per-wave workgroup, four key tiles
+constexpr int LEAD_BLOCKS = 2;         // query blocks of every head scheduled before the head groups
 constexpr int MAX_LAYOUT_BLOCKS = 8192;
 
 struct BlockArgs {
@@ -207,6 +208,18 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         const int rem = id - rank * (BH * sa.n_split);
         split = rem / BH;
         bh = rem - split * BH;
+    } else if (BLK && hg > 0) {
+        // block layouts: the first LEAD_BLOCKS query blocks of every head go first (the
+        // global tokens of BigBird- and Longformer-style layouts sit there, and those rows
+        // see every key block), then the rest in head groups
+        const int P = min(LEAD_BLOCKS, nqt);
+        if (id < P * BH) {
+            rank = id / BH;
+            bh = id - rank * BH;
+        } else {
+            grouped_order(id - P * BH, BH, nqt - P, hg, rank, bh);
+            rank += P;
+        }
     } else {
         grouped_order(id, BH, nqt, hg, rank, bh);
     }
@@ -928,6 +941,10 @@ int attn_launch_block_bf16(const AttnLaunch& a, const uint8_t* layout, int causa
     ba.nb = (a.N + BLOCK_TOKENS - 1) / BLOCK_TOKENS;
     const int BH = a.B * a.H;
     const unsigned grid = (unsigned)((long long)ba.nb * BH);
+    // head groups after the leading blocks: BigBird H32 N32768 +2%, a uniform random
+    // layout (10% of blocks) B2 H32 N16384 +12%
+    int hg = head_group_override();
+    if (hg < 0) hg = head_group(a.N, a.d);
     hipStream_t st = (hipStream_t)a.stream;
     const __bf16 *q = (const __bf16*)a.q, *k = (const __bf16*)a.k, *v = (const __bf16*)a.v;
     __bf16* o = (__bf16*)a.out;
@@ -935,17 +952,17 @@ int attn_launch_block_bf16(const AttnLaunch& a, const uint8_t* layout, int causa
     if (a.d == 128) {
         if (causal)
             hipLaunchKernelGGL((fwd_kernel<128, 1, 1, MASK_BLOCK_CAUSAL>), dim3(grid), dim3(NT), 0, st, q, k, v, o, a.lse,
-                               BH, a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba);
+                               BH, a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba, hg);
         else
             hipLaunchKernelGGL((fwd_kernel<128, 1, 1, MASK_BLOCK>), dim3(grid), dim3(NT), 0, st, q, k, v, o, a.lse, BH,
-                               a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba);
+                               a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba, hg);
     } else {
         if (causal)
             hipLaunchKernelGGL((fwd_kernel<64, 1, 1, MASK_BLOCK_CAUSAL>), dim3(grid), dim3(NT), 0, st, q, k, v, o, a.lse,
-                               BH, a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba);
+                               BH, a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba, hg);
         else
             hipLaunchKernelGGL((fwd_kernel<64, 1, 1, MASK_BLOCK>), dim3(grid), dim3(NT), 0, st, q, k, v, o, a.lse, BH,
-                               a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba);
+                               a.N, ba.nb, a.c_log2, a.negate_q, 0, SplitArgs{}, ba, hg);
     }
     return 0;
 }

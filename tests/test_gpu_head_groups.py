@@ -68,3 +68,14 @@ def test_backward_batches_partial_group():
 def test_forward_long_natural_partial_group():
     # 16 MB of K and V per head: the library's own choice is groups of 8
     run_case(1, 11, 32768, 128, "bf16", "causal", seed=5, n_rows=48, name="hgroup-long", gen_device="cuda")
+
+
+@pytest.mark.parametrize("B,H", [(1, 11), (3, 5)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_sparse_lead_blocks_and_groups(B, H, causal):
+    # block layouts: two leading query blocks of every head, then groups of 8 heads (partial last group)
+    from exact_blockwise_attention_attn_amd.inputs import random_block_layout
+    from tests.test_gpu_block_sparse import run_bs
+    lay = random_block_layout(H, 8, 0.4, seed=B + H, empty_rows=(3,))
+    with forced_head_group(8):
+        run_bs(B, H, 1000, 128, lay, causal, seed=B * 10 + H, name="bs-hgroup")
