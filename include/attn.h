@@ -82,7 +82,9 @@ enum attn_status {
  * Tile shape: bf16 calls pick 64 or 32 query rows per wave from the shape (32 for a
  * grid too small to fill the device twice or a window narrower than 4096 keys);
  * setting the environment variable ATTN_BF16_ROWS_PER_WAVE to 32 or 64 forces one.  Both
- * compute the same result.
+ * compute the same result.  Workgroups run in groups of heads whose K and V fit in
+ * half the device's 256 MB Infinity Cache; ATTN_HEAD_GROUP=n (0: one group) forces
+ * the group size, again without changing a result.
  *
  * Errors: returns ATTN_OK (0) or a negative attn_status.  Argument errors are
  * detected on the host before anything is enqueued, so nothing is written on such
