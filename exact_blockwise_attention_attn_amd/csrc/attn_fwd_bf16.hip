@@ -899,15 +899,20 @@ static int device_cus() {
 
 // Rows per wave: 64 (two 32-row blocks: each K/V operand read feeds two matrix
 // instructions) unless that leaves the grid short of two workgroups per compute
-// unit, or the mask is a narrow band, where 32 rows per wave win: half the key tiles
-// a workgroup spans outside its band, twice the workgroups, and a register budget
-// that fits two waves per SIMD.
+// unit, the mask is a band (2w + 1 <= 8193 keys, or a causal window w <= 8192), or the
+// mask is causal over at most 8192 keys.  There 32 rows per wave win: half the key
+// tiles a workgroup spans outside its band or past the diagonal, twice the
+// workgroups, and a register budget that fits two waves per SIMD (interleaved A/B on
+// one box: causal N4096-6144 +7%, N8192 +1.5%; window w4096 +3%; causal window w4096
+// +7%, w8192 +3%).
 int attn_launch_bf16(const AttnLaunch& a) {
     using namespace attn_bf16;
     const long long grid64 = (long long)((a.N + 255) / 256) * a.B * a.H;
-    const bool narrow_band = (a.mask_kind == ATTN_MASK_WINDOW && 2LL * a.window + 1 < 4096 && a.window < a.N - 1) ||
-                             (a.mask_kind == ATTN_MASK_CAUSAL_WINDOW && a.window + 1 < 2048 && a.window < a.N - 1);
-    bool rows32 = narrow_band || grid64 < 2LL * device_cus();
+    const bool band = (a.mask_kind == ATTN_MASK_WINDOW && 2LL * a.window + 1 <= 8193 && a.window < a.N - 1) ||
+                      (a.mask_kind == ATTN_MASK_CAUSAL_WINDOW && a.window <= 8192 && a.window < a.N - 1);
+    const bool short_causal = (a.mask_kind == ATTN_MASK_CAUSAL ||
+                               (a.mask_kind == ATTN_MASK_CAUSAL_WINDOW && a.window >= a.N - 1)) && a.N <= 8192;
+    bool rows32 = band || short_causal || grid64 < 2LL * device_cus();
     // explicit choice (both variants compute the same result; tests run each)
     if (const char* f = getenv("ATTN_BF16_ROWS_PER_WAVE")) {
         if (f[0] == '3' && f[1] == '2' && f[2] == 0) rows32 = true;
