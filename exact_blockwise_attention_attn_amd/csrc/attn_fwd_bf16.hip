@@ -902,9 +902,9 @@ static int device_cus() {
 // unit, the mask is a band (2w + 1 <= 8193 keys, or a causal window w <= 8192), or the
 // mask is causal over at most 8192 keys.  There 32 rows per wave win: half the key
 // tiles a workgroup spans outside its band or past the diagonal, twice the
-// workgroups, and a register budget that fits two waves per SIMD (interleaved A/B on
-// one box: causal N4096-6144 +7%, N8192 +1.5%; window w4096 +3%; causal window w4096
-// +7%, w8192 +3%).
+// workgroups, and a register budget that fits two waves per SIMD (interleaved A/B
+// timing on one MI355X: causal N4096-6144 +7%, N8192 +1.5%; window w4096 +3%;
+// causal window w4096 +7%, w8192 +3%).
 int attn_launch_bf16(const AttnLaunch& a) {
     using namespace attn_bf16;
     const long long grid64 = (long long)((a.N + 255) / 256) * a.B * a.H;
