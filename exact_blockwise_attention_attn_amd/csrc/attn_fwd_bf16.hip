@@ -908,19 +908,21 @@ static int device_cus() {
 
 // Rows per wave: 64 (two 32-row blocks: each K/V operand read feeds two matrix
 // instructions) unless that leaves the grid short of two workgroups per compute
-// unit, the mask is a band (2w + 1 <= 8193 keys, or a causal window w <= 8192), or the
-// mask is causal over fewer than 8192 keys.  There 32 rows per wave win: half the key
-// tiles a workgroup spans outside its band or past the diagonal, twice the
-// workgroups, and a register budget that fits two waves per SIMD (interleaved A/B
-// timing on one MI355X: causal N4096-6144 +4-10%, window w4096 +3%, causal window
-// w4096 +7%, w8192 +3%; at N8192 causal 64 rows per wave lead by 0.5-2%).
+// unit, the mask is a band (2w + 1 <= 8193 keys, or a causal window w <= 8192), or
+// the mask is causal over fewer than 8192 keys (16384 at d = 64).  There 32 rows per
+// wave win: half the key tiles a workgroup spans outside its band or past the
+// diagonal, twice the workgroups, and a register budget that fits two waves per SIMD
+// (interleaved A/B timing on one MI355X: causal N4096-6144 +4-10%, window w4096 +3%,
+// causal window w4096 +7%, w8192 +3%, causal d = 64 N8192 +3%; at N8192 causal
+// d = 128, 64 rows per wave lead by 0.5-2%).
 int attn_launch_bf16(const AttnLaunch& a) {
     using namespace attn_bf16;
     const long long grid64 = (long long)((a.N + 255) / 256) * a.B * a.H;
     const bool band = (a.mask_kind == ATTN_MASK_WINDOW && 2LL * a.window + 1 <= 8193 && a.window < a.N - 1) ||
                       (a.mask_kind == ATTN_MASK_CAUSAL_WINDOW && a.window <= 8192 && a.window < a.N - 1);
     const bool short_causal = (a.mask_kind == ATTN_MASK_CAUSAL ||
-                               (a.mask_kind == ATTN_MASK_CAUSAL_WINDOW && a.window >= a.N - 1)) && a.N < 8192;
+                               (a.mask_kind == ATTN_MASK_CAUSAL_WINDOW && a.window >= a.N - 1)) &&
+                              a.N < (a.d == 64 ? 16384 : 8192);
     bool rows32 = band || short_causal || grid64 < 2LL * device_cus();
     // explicit choice (both variants compute the same result; tests run each)
     if (const char* f = getenv("ATTN_BF16_ROWS_PER_WAVE")) {
