@@ -43,11 +43,13 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense bf16 MFMA; fp32
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = "exact_blockwise_attention_attn_amd/csrc/"
-# the sources each measured workload runs: a traffic record stays valid while they are unchanged
+# the sources each measured workload runs (and the build script, which holds their
+# compiler flags): a traffic record stays valid while they are unchanged
+BUILD = "exact_blockwise_attention_attn_amd/_build.py"
 KERNEL_SOURCES = {
-    "fwd": [CSRC + "attn_fwd_bf16.hip", CSRC + "attn_tile.h"],
-    "decode": [CSRC + "attn_decode_bf16.hip", CSRC + "attn_fwd_bf16.hip"],
-    "bwd": [CSRC + "attn_bwd_bf16.hip", CSRC + "attn_tile.h"],
+    "fwd": [CSRC + "attn_fwd_bf16.hip", CSRC + "attn_tile.h", BUILD],
+    "decode": [CSRC + "attn_decode_bf16.hip", CSRC + "attn_fwd_bf16.hip", BUILD],
+    "bwd": [CSRC + "attn_bwd_bf16.hip", CSRC + "attn_tile.h", BUILD],
 }
 
 

@@ -34,7 +34,12 @@ COMMON = [
 # Per-source flags.  The bf16 kernel never produces or consumes NaN (masked scores
 # are -inf, every row has an allowed key), so NaN-quieting canonicalisations can go
 # and the row maximum maps onto v_max3_f32.
-PER_SOURCE = {"attn_fwd_bf16.hip": ["-fno-honor-nans"], "attn_bwd_bf16.hip": ["-fno-honor-nans"]}
+# attn_bwd_bf16.hip: matrix-instruction accumulators in VGPRs.  Left to choose, the
+# compiler puts the dQ kernel's score and dP accumulators in AGPRs and copies all 32
+# of them to VGPRs on every key tile for the vector work (352 copies in the kernel);
+# with this form it uses 200 VGPRs, no AGPRs and no copies, at the same occupancy.
+PER_SOURCE = {"attn_fwd_bf16.hip": ["-fno-honor-nans"],
+              "attn_bwd_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, extra: list[str]) -> str:
