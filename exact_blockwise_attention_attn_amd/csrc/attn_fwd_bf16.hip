@@ -11,10 +11,12 @@
 // overflow is the source of NaN; work relative to the maximum, in log space).
 //
 // Work decomposition.  One workgroup of four waves (one per SIMD) per (batch*head,
-// block of BR = 256 query rows); each wave owns 64 rows (two 32-row blocks).  The
-// workgroup walks the key tiles (BC = 32 keys) that hold an allowed key for one of
-// its rows; tiles wholly outside the mask are never visited and element masking
-// runs only on tiles that straddle the mask or the sequence end.
+// block of BR = 128 QB query rows); each wave owns QB 32-row blocks: QB = 2 (one
+// workgroup per CU) or QB = 1 (two per CU, two waves per SIMD), chosen by shape.
+// Workgroups run in groups of heads whose K and V fit in the Infinity Cache
+// (grouped_order).  The workgroup walks the key tiles (BC = 32 keys) that hold an
+// allowed key for one of its rows; tiles wholly outside the mask are never visited
+// and element masking runs only on tiles that straddle the mask or the sequence end.
 //
 // K/V staging.  Each K and V tile goes HBM -> LDS directly (global_load_lds_dwordx4,
 // no VGPR round trip), row-major with the 16-byte chunks of a row XOR-swizzled by
@@ -28,8 +30,8 @@
 // previous one, the vector ALUs the softmax of this one, and the LDS reads fetch
 // the matrix operands a few instructions ahead.  They are laid out by hand, one
 // matrix instruction per slot with a share of the softmax behind it, and the
-// compiler's scheduler is fenced between slots, so the two kinds of work of the
-// single wave on each SIMD overlap.
+// compiler's scheduler is fenced between slots, so the two kinds of work of a wave
+// overlap (at QB = 1 a second wave on the SIMD adds its own).
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, 64-wide wavefront).  Each wave
 // computes the transposed score block S^T = K_tile Q_w^T (keys x queries), so a
