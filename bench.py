@@ -47,7 +47,7 @@ CSRC = "exact_blockwise_attention_attn_amd/csrc/"
 # compiler flags): a traffic record stays valid while they are unchanged
 BUILD = "exact_blockwise_attention_attn_amd/_build.py"
 KERNEL_SOURCES = {
-    "fwd": [CSRC + "attn_fwd_bf16.hip", CSRC + "attn_tile.h", BUILD],
+    "fwd": [CSRC + "attn_fwd_bf16.hip", CSRC + "attn_fwd_bf16_d64.hip", CSRC + "attn_tile.h", BUILD],
     "decode": [CSRC + "attn_decode_bf16.hip", CSRC + "attn_fwd_bf16.hip", BUILD],
     "bwd": [CSRC + "attn_bwd_bf16.hip", CSRC + "attn_tile.h", BUILD],
 }

@@ -18,7 +18,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip", "attn_decode_bf16.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_bf16_d64.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip",
+           "attn_decode_bf16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -38,8 +39,12 @@ COMMON = [
 # compiler puts the dQ kernel's score and dP accumulators in AGPRs and copies all 32
 # of them to VGPRs on every key tile for the vector work (352 copies in the kernel);
 # with this form it uses 200 VGPRs, no AGPRs and no copies, at the same occupancy.
+# attn_fwd_bf16_d64.hip (the dense d = 64 forward kernels): the same form lifts their
+# occupancy; the d = 128 forward kernels stay in the default form.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 PER_SOURCE = {"attn_fwd_bf16.hip": ["-fno-honor-nans"],
-              "attn_bwd_bf16.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
+              "attn_fwd_bf16_d64.hip": ["-fno-honor-nans", *VGPR_FORM],
+              "attn_bwd_bf16.hip": ["-fno-honor-nans", *VGPR_FORM]}
 
 
 def _compile(src: str, extra: list[str]) -> str:

@@ -895,6 +895,15 @@ static int by_mask(const AttnLaunch& a) {
 
 }  // namespace attn_bf16
 
+#ifdef ATTN_FWD_D64_TU
+// The dense d = 64 kernels, compiled in a translation unit of their own
+// (attn_fwd_bf16_d64.hip) with matrix-instruction accumulators in VGPRs.
+int attn_launch_bf16_d64(const AttnLaunch& a, bool rows32) {
+    using namespace attn_bf16;
+    return rows32 ? by_mask<64, 1, 1>(a) : by_mask<64, 2, 1>(a);
+}
+#else
+
 // Compute units of the current device (cached per device; the value never changes).
 static int device_cus() {
     static std::atomic<int> cache[64];
@@ -932,7 +941,7 @@ int attn_launch_bf16(const AttnLaunch& a) {
         if (f[0] == '6' && f[1] == '4' && f[2] == 0) rows32 = false;
     }
     if (a.d == 128) return rows32 ? by_mask<128, 1, 1>(a) : by_mask<128, 2, 1>(a);
-    return rows32 ? by_mask<64, 1, 1>(a) : by_mask<64, 2, 1>(a);
+    return attn_launch_bf16_d64(a, rows32);
 }
 
 // Key ranges for the split-KV path: enough workgroups to fill the 256 CUs twice, at
@@ -1024,3 +1033,5 @@ int attn_launch_kv_bf16(const AttnLaunch& a, int Nk, int q_offset, float* part_o
     if (a.d == 128) return by_mask_split<128>(a, sa);
     return by_mask_split<64>(a, sa);
 }
+
+#endif  // ATTN_FWD_D64_TU

@@ -39,6 +39,7 @@ struct AttnBwdLaunch {
 };
 
 int attn_launch_bf16(const AttnLaunch& a);
+int attn_launch_bf16_d64(const AttnLaunch& a, bool rows32);   // dense d = 64 (attn_fwd_bf16_d64.hip)
 int attn_launch_bwd_bf16(const AttnBwdLaunch& a);
 int attn_launch_f32(const AttnLaunch& a);
 

@@ -15,7 +15,6 @@ import pytest
 from exact_blockwise_attention_attn_amd import _build
 from tests import isa_hazards
 
-SRC = os.path.join(_build.CSRC, "attn_fwd_bf16.hip")
 
 
 def test_checker_finds_planted_hazard():
@@ -73,18 +72,21 @@ def test_checker_ignores_value_replaced_by_mfma():
 
 
 @pytest.mark.skipif(shutil.which(_build.HIPCC) is None and not os.path.exists(_build.HIPCC), reason="hipcc not found")
-def test_bf16_kernel_asm_mfma_sources_not_written_by_valu():
+# the d = 128 kernels (4 masks x (rows per wave {32, 64}, plus the split-KV mode at 32)
+# + the two block-layout kinds) and the d = 64 split-KV and block-layout kernels live in
+# attn_fwd_bf16.hip; the dense d = 64 kernels (4 masks x rows per wave {32, 64}) in
+# attn_fwd_bf16_d64.hip, built with its own flags
+@pytest.mark.parametrize("src,count", [("attn_fwd_bf16.hip", 20), ("attn_fwd_bf16_d64.hip", 8)])
+def test_bf16_kernel_asm_mfma_sources_not_written_by_valu(src, count):
     with tempfile.TemporaryDirectory() as tmp:
         out = os.path.join(tmp, "k.s")
-        cmd = [_build.HIPCC, *_build.COMMON, *_build.PER_SOURCE.get("attn_fwd_bf16.hip", []),
-               "-x", "hip", "-S", "--cuda-device-only", SRC, "-o", out]
+        cmd = [_build.HIPCC, *_build.COMMON, *_build.PER_SOURCE.get(src, []),
+               "-x", "hip", "-S", "--cuda-device-only", os.path.join(_build.CSRC, src), "-o", out]
         res = subprocess.run(cmd, capture_output=True, text=True)
         assert res.returncode == 0, res.stderr
         text = open(out, encoding="utf-8").read()
     names = re.findall(r"^(_ZN9attn_bf1610fwd_kernel\w+):", text, re.M)
-    # d in {64, 128} x (4 masks x (rows per wave {32, 64}, plus the split-KV mode at 32)
-    # + the two block-layout kinds at 32 rows per wave)
-    assert len(names) == 28
+    assert len(names) == count
     for name in names:
         body = text[text.index(name + ":"):]
         body = body[:body.index(".Lfunc_end")]      # the whole function (early exits included)
