@@ -11,4 +11,4 @@ from ._lib import (  # noqa: F401
     bwd, fwd, fwd_block_sparse, fwd_kv, load,
 )
 
-__version__ = "0.4.0"
+__version__ = "0.5.0"

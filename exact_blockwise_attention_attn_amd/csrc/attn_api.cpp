@@ -259,6 +259,6 @@ extern "C" const char* attn_strerror(int status) {
 }
 
 extern "C" const char* attn_version(void) {
-    return "attn 0.4.0 (gfx950; forward bf16 v_mfma_f32_32x32x16_bf16 and fp32 VALU; block-sparse forward bf16; "
+    return "attn 0.5.0 (gfx950; forward bf16 v_mfma_f32_32x32x16_bf16 and fp32 VALU; block-sparse forward bf16; "
            "split-KV forward and decode bf16; backward bf16)";
 }
