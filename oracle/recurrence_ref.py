@@ -36,7 +36,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention_ref import MASK_CAUSAL, MASK_NONE, MASK_WINDOW, allowed_mask
+from .attention_ref import MASK_CAUSAL, MASK_CAUSAL_WINDOW, MASK_NONE, MASK_WINDOW, allowed_mask
 
 
 def kv_tile_range(q0, q1, n_keys, block_cols, mask_kind, window):
@@ -51,11 +51,23 @@ def kv_tile_range(q0, q1, n_keys, block_cols, mask_kind, window):
         lo_key = max(0, q0 - window)
         hi_key = min(n_keys - 1, q1 - 1 + window)
         return lo_key // block_cols, hi_key // block_cols
+    if mask_kind == MASK_CAUSAL_WINDOW:
+        # the causal half of the band ("长序列推理中的注意力机制优化策略与实践", §2.1):
+        # row i sees keys i - w .. i, so the block's keys run from its first row's
+        # lowest key to its last row's own position
+        lo_key = max(0, q0 - window)
+        hi_key = min(n_keys - 1, q1 - 1)
+        return lo_key // block_cols, hi_key // block_cols
     raise ValueError(f"unknown mask kind {mask_kind}")
 
 
 def _round_bf16(x: np.ndarray) -> np.ndarray:
-    """Round float64 values to the nearest bf16 (ties to even) via float32."""
+    """Round values to bf16 the way a kernel holding them in float32 does: first to
+    float32 (nearest, ties to even), then to the nearest bf16 (8 significant bits),
+    ties to the neighbour whose last kept bit is 0.  Adding 0x7FFF plus the last
+    kept bit to the float32 pattern and clearing the low 16 bits does exactly that,
+    a carry out of the kept bits stepping into the exponent (1.99609375 -> 2.0).
+    Finite inputs only (the probabilities are finite and >= 0)."""
     f = x.astype(np.float32)
     u = f.view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
