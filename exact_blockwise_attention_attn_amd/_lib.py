@@ -69,6 +69,8 @@ def load():
     lib.attn_fwd_block_sparse.restype = i
     lib.attn_fwd_block_sparse_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i]
     lib.attn_fwd_block_sparse_check_args.restype = i
+    lib.attn_set_schedule.argtypes = [i, i]
+    lib.attn_set_schedule.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -127,12 +129,53 @@ def attn_fwd_block_sparse_check_args(q, k, v, out, lse, B, H, N, d, scale, causa
     return load().attn_fwd_block_sparse_check_args(q, k, v, out, lse, B, H, N, d, scale, causal, layout, dtype)
 
 
+def attn_set_schedule(rows_per_wave: int, head_group: int) -> int:
+    """C ``attn_set_schedule``: force the bf16 tile shape (32 / 64 rows per wave, 0 =
+    the library's choice) and head-group size (n, 0 = one group, -1 = the library's
+    choice) for later calls; returns the status code."""
+    return load().attn_set_schedule(rows_per_wave, head_group)
+
+
 def attn_strerror(status: int) -> str:
     return load().attn_strerror(status).decode()
 
 
 def attn_version() -> str:
     return load().attn_version().decode()
+
+
+def _same_device(dev, **tensors):
+    """Every named tensor must be a device tensor on ``dev`` (a host tensor's
+    pointer would reach the kernels as is)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not getattr(t, "is_cuda", False) or t.device != dev:
+            raise ValueError(f"{name} must be a device tensor on {dev}")
+
+
+def _like(name, t, shape, dtype):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+
+
+def _stream(stream, dev):
+    """(torch stream object, raw hipStream_t) for ``stream``: None for torch's
+    current stream on ``dev``, a torch stream, or a raw handle as an int.  The
+    binding allocates its temporaries and outputs on that stream, so torch's caching
+    allocator never hands their memory to other work while the kernels that use them
+    are still queued there."""
+    import torch
+
+    if stream is None:
+        s = torch.cuda.current_stream(dev)
+    elif isinstance(stream, torch.cuda.Stream):
+        s = stream
+    else:
+        h = int(stream)
+        s = torch.cuda.default_stream(dev) if h == torch.cuda.default_stream(dev).cuda_stream \
+            else torch.cuda.ExternalStream(h, device=dev)
+    return s, s.cuda_stream
 
 
 def fwd(q, k, v, mask="none", window=0, scale=None, out=None, lse=None, stream=None):
@@ -147,29 +190,29 @@ def fwd(q, k, v, mask="none", window=0, scale=None, out=None, lse=None, stream=N
         raise ValueError("q, k, v must be [B, H, N, d] tensors of one shape")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q, k, v must all be bfloat16 or all float32")
-    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+    if not getattr(q, "is_cuda", False):
         raise ValueError("q, k, v must be device tensors")
+    _same_device(q.device, k=k, v=v, out=out, lse=lse)
     for t in (q, k, v):
         if not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous")
     B, H, N, d = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if out is not None:
+        _like("out", out, q.shape, q.dtype)
+    if lse is not None:
+        _like("lse", lse, (B, H, N), torch.float32)
     if scale is None:
         scale = d ** -0.5
     mk = MASKS[mask] if isinstance(mask, str) else int(mask)
     dt = ATTN_DTYPE_BF16 if q.dtype == torch.bfloat16 else ATTN_DTYPE_F32
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
+    s, raw = _stream(stream, q.device)
+    with torch.cuda.device(q.device), torch.cuda.stream(s):
+        if out is None:
+            out = torch.empty_like(q)
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
         st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                      B, H, N, d, float(scale), mk, int(window), dt, stream)
+                      B, H, N, d, float(scale), mk, int(window), dt, raw)
     if st != ATTN_OK:
         raise AttnError(st, attn_strerror(st))
     return out, lse
@@ -188,26 +231,28 @@ def bwd(q, k, v, out, dout, lse, mask="none", window=0, scale=None, dq=None, dk=
         raise ValueError("q, k, v, out, dout must be [B, H, N, d] tensors of one shape")
     if any(t.dtype != torch.bfloat16 for t in ts):
         raise ValueError("the backward takes bfloat16 tensors")
-    if not all(t.is_cuda and t.is_contiguous() for t in ts) or not (lse.is_cuda and lse.is_contiguous()):
+    if not getattr(q, "is_cuda", False):
+        raise ValueError("inputs must be contiguous device tensors")
+    _same_device(q.device, k=k, v=v, out=out, dout=dout, lse=lse, dq=dq, dk=dk, dv=dv)
+    if not all(t.is_contiguous() for t in ts) or not lse.is_contiguous():
         raise ValueError("inputs must be contiguous device tensors")
     B, H, N, d = q.shape
     if lse.shape != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be a float32 [B, H, N] tensor")
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(q) if dk is None else dk
-    dv = torch.empty_like(q) if dv is None else dv
-    for g in (dq, dk, dv):
-        if g.shape != q.shape or g.dtype != q.dtype or not g.is_contiguous():
-            raise ValueError("dq, dk, dv must be contiguous tensors like q")
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if g is not None:
+            _like(name, g, q.shape, q.dtype)
     if scale is None:
         scale = d ** -0.5
     mk = MASKS[mask] if isinstance(mask, str) else int(mask)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
+    s, raw = _stream(stream, q.device)
+    with torch.cuda.device(q.device), torch.cuda.stream(s):
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(q) if dk is None else dk
+        dv = torch.empty_like(q) if dv is None else dv
         st = attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), mk, int(window),
-                      ATTN_DTYPE_BF16, stream)
+                      ATTN_DTYPE_BF16, raw)
     if st != ATTN_OK:
         raise AttnError(st, attn_strerror(st))
     return dq, dk, dv
@@ -227,32 +272,36 @@ def fwd_kv(q, k, v, q_offset=None, mask="none", window=0, scale=None, out=None, 
         raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
     if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
         raise ValueError("attn_fwd_kv takes bfloat16 tensors")
-    if not all(t.is_cuda and t.is_contiguous() for t in (q, k, v)):
+    if not getattr(q, "is_cuda", False):
+        raise ValueError("q, k, v must be contiguous device tensors")
+    _same_device(q.device, k=k, v=v, out=out, lse=lse, workspace=workspace)
+    if not all(t.is_contiguous() for t in (q, k, v)):
         raise ValueError("q, k, v must be contiguous device tensors")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     if q_offset is None:
         q_offset = Nk - Nq
-    out = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor like q")
-    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor")
+    if out is not None:
+        _like("out", out, q.shape, q.dtype)
+    if lse is not None:
+        _like("lse", lse, (B, H, Nq), torch.float32)
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     need = attn_fwd_kv_workspace_size(B, H, Nq, Nk, d)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else 0
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if scale is None:
         scale = d ** -0.5
     mk = MASKS[mask] if isinstance(mask, str) else int(mask)
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
+    s, raw = _stream(stream, q.device)
+    with torch.cuda.device(q.device), torch.cuda.stream(s):
+        out = torch.empty_like(q) if out is None else out
+        if lse is None:
+            lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else 0
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         st = attn_fwd_kv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
-                         float(scale), mk, int(window), int(q_offset), ATTN_DTYPE_BF16, ws_ptr, ws_bytes, stream)
+                         float(scale), mk, int(window), int(q_offset), ATTN_DTYPE_BF16, ws_ptr, ws_bytes, raw)
     if st != ATTN_OK:
         raise AttnError(st, attn_strerror(st))
     return out, lse
@@ -270,24 +319,30 @@ def fwd_block_sparse(q, k, v, layout, causal=False, scale=None, out=None, lse=No
         raise ValueError("q, k, v must be [B, H, N, d] tensors of one shape")
     if any(t.dtype != torch.bfloat16 for t in (q, k, v)):
         raise ValueError("the block-sparse forward takes bfloat16 tensors")
-    if not all(t.is_cuda and t.is_contiguous() for t in (q, k, v, layout)):
+    if not getattr(q, "is_cuda", False):
+        raise ValueError("q, k, v and layout must be contiguous device tensors")
+    _same_device(q.device, k=k, v=v, layout=layout, out=out, lse=lse)
+    if not all(t.is_contiguous() for t in (q, k, v, layout)):
         raise ValueError("q, k, v and layout must be contiguous device tensors")
     B, H, N, d = q.shape
     nb = -(-N // ATTN_BLOCK_SPARSE_BLOCK)
-    if layout.dtype == torch.bool:
-        layout = layout.to(torch.uint8)
-    if layout.dtype != torch.uint8 or tuple(layout.shape) != (H, nb, nb):
-        raise ValueError(f"layout must be a uint8 tensor [H, {nb}, {nb}]")
-    out = torch.empty_like(q) if out is None else out
-    if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if layout.dtype not in (torch.bool, torch.uint8) or tuple(layout.shape) != (H, nb, nb):
+        raise ValueError(f"layout must be a uint8 (or bool) tensor [H, {nb}, {nb}]")
+    if out is not None:
+        _like("out", out, q.shape, q.dtype)
+    if lse is not None:
+        _like("lse", lse, (B, H, N), torch.float32)
     if scale is None:
         scale = d ** -0.5
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    with torch.cuda.device(q.device):
+    s, raw = _stream(stream, q.device)
+    with torch.cuda.device(q.device), torch.cuda.stream(s):
+        if layout.dtype == torch.bool:
+            layout = layout.to(torch.uint8)     # the copy runs on the launch stream, before the kernel
+        out = torch.empty_like(q) if out is None else out
+        if lse is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
         st = attn_fwd_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N,
-                                   d, float(scale), 1 if causal else 0, layout.data_ptr(), ATTN_DTYPE_BF16, stream)
+                                   d, float(scale), 1 if causal else 0, layout.data_ptr(), ATTN_DTYPE_BF16, raw)
     if st != ATTN_OK:
         raise AttnError(st, attn_strerror(st))
     return out, lse

@@ -447,7 +447,7 @@ static int launch(const AttnBwdLaunch& a) {
     // d128 +11%, B2 H32 N8192 +2%; a window's blocks read a narrow band, where the
     // grouping measured 3% slower
     const bool band = MASK == ATTN_MASK_WINDOW || MASK == ATTN_MASK_CAUSAL_WINDOW;
-    int hg = head_group_override();
+    int hg = attn_sched_head_group();
     if (hg < 0) hg = band ? 0 : head_group(a.N, a.d);
     const long long rows = (long long)a.B * a.H * a.N;
     constexpr int RPB = 4 * (64 / (D / 8));            // rows per prep workgroup

@@ -61,7 +61,6 @@
 #include <stdint.h>
 
 #include <atomic>
-#include <cstdlib>
 
 #include "attn_launch.h"
 #include "attn_tile.h"
@@ -796,7 +795,7 @@ static int launch(const AttnLaunch& a) {
     using C = Cfg<D, QB, KB>;
     const int nqt = (a.N + C::BR - 1) / C::BR;
     const long long grid = (long long)nqt * a.B * a.H;
-    int hg = head_group_override();
+    int hg = attn_sched_head_group();
     if (hg < 0) hg = head_group(a.N, a.d);      // K and V of a head: causal B4 H32 N16384 d128 +12%
     hipLaunchKernelGGL((fwd_kernel<D, QB, KB, MASK>), dim3((unsigned)grid), dim3(C::NT), 0, (hipStream_t)a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.out, a.lse,
@@ -936,10 +935,8 @@ int attn_launch_bf16(const AttnLaunch& a) {
                               a.N < (a.d == 64 ? 16384 : 8192);
     bool rows32 = band || short_causal || grid64 < 2LL * device_cus();
     // explicit choice (both variants compute the same result; tests run each)
-    if (const char* f = getenv("ATTN_BF16_ROWS_PER_WAVE")) {
-        if (f[0] == '3' && f[1] == '2' && f[2] == 0) rows32 = true;
-        if (f[0] == '6' && f[1] == '4' && f[2] == 0) rows32 = false;
-    }
+    const int forced = attn_sched_rows_per_wave();
+    if (forced) rows32 = forced == 32;
     if (a.d == 128) return rows32 ? by_mask<128, 1, 1>(a) : by_mask<128, 2, 1>(a);
     return attn_launch_bf16_d64(a, rows32);
 }
@@ -970,7 +967,7 @@ int attn_launch_block_bf16(const AttnLaunch& a, const uint8_t* layout, int causa
     const unsigned grid = (unsigned)((long long)ba.nb * BH);
     // head groups after the leading blocks: BigBird H32 N32768 +2%, a uniform random
     // layout (10% of blocks) B2 H32 N16384 +12%
-    int hg = head_group_override();
+    int hg = attn_sched_head_group();
     if (hg < 0) hg = head_group(a.N, a.d);
     hipStream_t st = (hipStream_t)a.stream;
     const __bf16 *q = (const __bf16*)a.q, *k = (const __bf16*)a.k, *v = (const __bf16*)a.v;

@@ -5,7 +5,6 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <stdlib.h>
 
 namespace attn_tile {
 
@@ -46,16 +45,6 @@ inline int head_group(int N, int d) {
     const long long per_head = 2LL * N * d * 2;
     const long long fit = (128LL << 20) / (8 * per_head);
     return 8 * (int)(fit < 1 ? 1 : (fit > (1 << 20) ? (1 << 20) : fit));
-}
-
-// Explicit group size from the environment (ATTN_HEAD_GROUP = n >= 0, 0 for one
-// group of every head), -1 when unset.  Every order computes the same result; the
-// tests force small groups to run the partial last group at small sizes.
-inline int head_group_override() {
-    const char* e = getenv("ATTN_HEAD_GROUP");
-    if (!e || !*e) return -1;
-    const int v = atoi(e);
-    return v >= 0 ? v : -1;
 }
 
 template <int I, int N, typename F>

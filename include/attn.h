@@ -80,11 +80,9 @@ enum attn_status {
  * calls and may be called concurrently from several host threads.
  *
  * Tile shape: bf16 calls pick 64 or 32 query rows per wave from the shape (32 for a
- * grid too small to fill the device twice or a window narrower than 4096 keys);
- * setting the environment variable ATTN_BF16_ROWS_PER_WAVE to 32 or 64 forces one.  Both
- * compute the same result.  Workgroups run in groups of heads whose K and V fit in
- * half the device's 256 MB Infinity Cache; ATTN_HEAD_GROUP=n (0: one group) forces
- * the group size, again without changing a result.
+ * grid too small to fill the device twice or a window narrower than 4096 keys), and
+ * run workgroups in groups of heads whose K and V fit in half the device's 256 MB
+ * Infinity Cache.  attn_set_schedule forces either choice; no choice changes a result.
  *
  * Errors: returns ATTN_OK (0) or a negative attn_status.  Argument errors are
  * detected on the host before anything is enqueued, so nothing is written on such
@@ -245,6 +243,25 @@ int attn_fwd_block_sparse(const void* q, const void* k, const void* v, void* out
 int attn_fwd_block_sparse_check_args(const void* q, const void* k, const void* v, const void* out,
                                      const float* lse, int B, int H, int N, int d, float scale, int causal,
                                      const unsigned char* layout, int dtype);
+
+/*
+ * attn_set_schedule - force the schedule choices the library otherwise makes from
+ * the shape, process-wide, for every later call (a tuning and test switch, not part
+ * of the operation: every setting computes the same result, bit for bit for a
+ * given tile shape).
+ *
+ *   rows_per_wave  query rows per wave of the bf16 forward kernels: 32 or 64, or 0
+ *                  for the library's own choice.
+ *   head_group     heads per workgroup group of the bf16 forward and backward
+ *                  kernels (groups run one after another so that their K and V stay
+ *                  in the Infinity Cache): n >= 1 heads, 0 for a single group of
+ *                  every head, or -1 for the library's own choice.
+ *
+ * Returns ATTN_OK, or ATTN_ERR_BAD_SHAPE for a value outside those sets (then
+ * nothing changes).  Safe to call from any thread; calls already enqueued keep the
+ * schedule they were launched with.
+ */
+int attn_set_schedule(int rows_per_wave, int head_group);
 
 /* attn_strerror - static, NUL-terminated text for a status code (never NULL). */
 const char* attn_strerror(int status);

@@ -129,23 +129,35 @@ def run_case(B, H, N, d, dtype, mask, window=0, scale=None, seed=0, q_mult=1.0, 
 ROWS_PER_WAVE = ("32", "64")
 
 
-class forced_rows_per_wave:
-    """Context manager: force the bf16 tile shape through the library's environment
-    switch (None leaves the library's own choice)."""
+_SCHED = {"rows_per_wave": 0, "head_group": -1}   # what attn_set_schedule was last given
 
-    def __init__(self, rpw):
-        self.rpw = rpw
-        self.old = None
+
+class _forced:
+    """Context manager: force one schedule choice of the library (rows per wave or
+    head-group size) through attn_set_schedule, restoring the previous one on exit.
+    Every choice computes the same result; the tests run each against one oracle."""
+
+    def __init__(self, key, value):
+        self.key, self.value, self.old = key, value, None
 
     def __enter__(self):
-        self.old = os.environ.get("ATTN_BF16_ROWS_PER_WAVE")
-        if self.rpw is not None:
-            os.environ["ATTN_BF16_ROWS_PER_WAVE"] = self.rpw
+        self.old = _SCHED[self.key]
+        if self.value is not None:
+            _SCHED[self.key] = int(self.value)
+            assert attn.attn_set_schedule(_SCHED["rows_per_wave"], _SCHED["head_group"]) == 0
         return self
 
     def __exit__(self, *exc):
-        if self.old is None:
-            os.environ.pop("ATTN_BF16_ROWS_PER_WAVE", None)
-        else:
-            os.environ["ATTN_BF16_ROWS_PER_WAVE"] = self.old
+        _SCHED[self.key] = self.old
+        assert attn.attn_set_schedule(_SCHED["rows_per_wave"], _SCHED["head_group"]) == 0
         return False
+
+
+def forced_rows_per_wave(rpw):
+    """Force 32 or 64 query rows per wave of the bf16 forward (None: the library's choice)."""
+    return _forced("rows_per_wave", rpw)
+
+
+def forced_head_group(g):
+    """Force the head-group size (n heads, 0 for one group; None: the library's choice)."""
+    return _forced("head_group", g)

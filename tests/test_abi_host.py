@@ -23,8 +23,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_check_args", "attn_check_args", "attn_fwd",
                                     "attn_fwd_block_sparse", "attn_fwd_block_sparse_check_args", "attn_fwd_kv",
-                                    "attn_fwd_kv_check_args", "attn_fwd_kv_workspace_size", "attn_strerror",
-                                    "attn_version"]
+                                    "attn_fwd_kv_check_args", "attn_fwd_kv_workspace_size", "attn_set_schedule",
+                                    "attn_strerror", "attn_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -276,3 +276,13 @@ def test_block_sparse_rejects_before_any_launch():
     assert attn.attn_fwd_block_sparse(q, k, v, o, l, 1, 1, 100, 96, 0.1, 0, lay, 1, None) == \
         _lib.ATTN_ERR_UNSUPPORTED_HEAD_DIM
     assert attn.attn_fwd_block_sparse(q, k, v, o, l, 1, 1, 100, 64, 0.1, 0, 0, 1, None) == _lib.ATTN_ERR_NULL_PTR
+
+
+def test_set_schedule_validates():
+    assert attn.attn_set_schedule(0, -1) == 0
+    for rpw, hg in ((32, 8), (64, 0), (0, 16)):
+        assert attn.attn_set_schedule(rpw, hg) == 0
+    for rpw, hg in ((16, -1), (128, -1), (-32, -1), (0, -2)):
+        assert attn.attn_set_schedule(rpw, hg) == _lib.ATTN_ERR_BAD_SHAPE
+    assert attn.attn_set_schedule(0, -1) == 0
+

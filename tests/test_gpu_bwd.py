@@ -98,3 +98,31 @@ def test_bwd_errors_leave_gradients_untouched():
         attn.bwd(q, k, v, out, out, lse, mask="causal", dq=dq, dk=q)      # dk aliases q
     torch.cuda.synchronize()
     assert torch.all(dq == 7.0)
+
+
+def test_bwd_benchmark_shape():
+    """The backward at the shape bench.py times (B2 H32 N8192 d128 causal) with the
+    library's own schedule (head groups of 32: two full groups), every gradient of
+    three whole heads against the float64 backward oracle: the first head, the
+    first head of the second group and the last head."""
+    B, H, N, d = 2, 32, 8192, 128
+    scale = float(np.float32(d ** -0.5))
+    say(f"[gpu] bwd-bench B{B} H{H} N{N} d{d} causal (library schedule)")
+    q, k, v = make_qkv(B, H, N, d, torch.bfloat16, seed=0, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(1000)
+    do = torch.randn((B, H, N, d), generator=g, device="cuda").to(torch.bfloat16)
+    out, lse = attn.fwd(q, k, v, mask="causal", scale=scale)
+    dq, dk, dv = attn.bwd(q, k, v, out, do, lse, mask="causal", scale=scale)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (1, 0), (1, 31)):
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        refs = attention_backward(to_np(q[sl]), to_np(k[sl]), to_np(v[sl]), to_np(do[sl]), scale, 1, 0)
+        for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+            gn = to_np(got[sl])
+            assert np.all(np.isfinite(gn)), f"head ({b},{h}): non-finite {name}"
+            err = float(np.abs(gn - ref).max())
+            mref = float(np.abs(ref).max())
+            rms = float(np.sqrt(np.sum((gn - ref) ** 2)) / max(np.sqrt(np.sum(ref ** 2)), 1e-30))
+            say(f"  head ({b},{h}) {name}: max|err|={err:.3e} max|ref|={mref:.3e} relRMS={rms:.3e}")
+            assert err <= TOL_MAX * max(1.0, mref), f"head ({b},{h}): {name} max|err| {err}"
+            assert rms <= TOL_RMS, f"head ({b},{h}): {name} relative RMS {rms}"

@@ -1,16 +1,14 @@
 """GPU parity of the grouped workgroup order (heads in groups, every query or key
 block of a group before the next): shapes whose (batch, head) count is not a
 multiple of the group size run a partial last group.  Small sizes force small
-groups through ATTN_HEAD_GROUP (the order never changes a result; the oracle is the
+groups through attn_set_schedule (the order never changes a result; the oracle is the
 same); one long case reaches a partial group with the library's own choice
 (K and V of 16 MB per head: groups of 8, 11 heads = 8 + 3)."""
-import os
-
 import numpy as np
 import pytest
 import torch
 
-from tests.gpu_util import require_gpu, run_case
+from tests.gpu_util import forced_head_group, require_gpu, run_case
 from tests.test_gpu_bwd import run_bwd
 
 pytestmark = pytest.mark.gpu
@@ -19,24 +17,6 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     require_gpu()
-
-
-class forced_head_group:
-    def __init__(self, g):
-        self.g = g
-        self.old = None
-
-    def __enter__(self):
-        self.old = os.environ.get("ATTN_HEAD_GROUP")
-        os.environ["ATTN_HEAD_GROUP"] = str(self.g)
-        return self
-
-    def __exit__(self, *exc):
-        if self.old is None:
-            os.environ.pop("ATTN_HEAD_GROUP", None)
-        else:
-            os.environ["ATTN_HEAD_GROUP"] = self.old
-        return False
 
 
 # (B, H): 11 heads = 8 + 3; 15 = 8 + 7; 16 = two full groups; 5 < one group
