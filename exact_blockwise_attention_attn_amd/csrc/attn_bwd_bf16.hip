@@ -89,15 +89,15 @@ struct Loader {
             row[i] = r;
         }
     }
-    // rows t*BT .. t*BT+BT-1 of a [N, D] head into dst; rows past the end reload row N-1
-    __device__ __forceinline__ void load(const __bf16* src, int t, int N, char* dst, int wave) const {
+    // rows t*BT .. t*BT+BT-1 of a [N, D] head (buffer resource `rs`, head_rsrc) into
+    // dst; rows past the end reload row N-1
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int t, int N, char* dst, int wave) const {
         const int r0 = t * BT;
-        const char* base = reinterpret_cast<const char*>(src + (size_t)r0 * D);
+        const uint32_t soff = (uint32_t)r0 * (uint32_t)(2 * D);
 #pragma unroll
         for (int i = 0; i < Shape<D>::LPW; ++i) {
             const uint32_t o = off[i] - (uint32_t)max(0, row[i] - (N - 1 - r0)) * (2 * D);
-            __builtin_amdgcn_global_load_lds((const void*)(base + o),
-                                             (lds_void*)(dst + (wave * Shape<D>::LPW + i) * 1024), 16, 0, 0);
+            dma16(rs, (lds_void*)(dst + (wave * Shape<D>::LPW + i) * 1024), o, soff);
         }
     }
 };
@@ -199,8 +199,10 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
         dd = *reinterpret_cast<const float*>(dscratch + ((size_t)bh * N + row) * D * 2);
     };
 
-    ld.load(Q + head, t_lo, N, qbuf0, wave);
-    ld.load(dO + head, t_lo, N, gbuf0, wave);
+    const __amdgpu_buffer_rsrc_t qrs = buffer_rsrc(Q + head, (uint32_t)N * (uint32_t)(2 * D));
+    const __amdgpu_buffer_rsrc_t grs = buffer_rsrc(dO + head, (uint32_t)N * (uint32_t)(2 * D));
+    ld.load(qrs, t_lo, N, qbuf0, wave);
+    ld.load(grs, t_lo, N, gbuf0, wave);
     if (wave == 0 && lane < BT) {
         float l2, dd;
         stage_load(t_lo, l2, dd);
@@ -224,8 +226,8 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
         const bool more = u + 1 < n_tiles;
         float l2n = 0.f, ddn = 0.f;
         if (more) {
-            ld.load(Q + head, t + 1, N, qn, wave);
-            ld.load(dO + head, t + 1, N, gn, wave);
+            ld.load(qrs, t + 1, N, qn, wave);
+            ld.load(grs, t + 1, N, gn, wave);
             if (wave == 0 && lane < BT) stage_load(t + 1, l2n, ddn);
         }
         // S = Q_t K^T and dP = dO_t V^T: rows = the tile's queries, columns = keys (lanes)
@@ -368,8 +370,10 @@ void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqa[j][r] = 0.f;
 
-    ld.load(K + head, t_lo, N, kbuf0, wave);
-    ld.load(V + head, t_lo, N, vbuf0, wave);
+    const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(K + head, (uint32_t)N * (uint32_t)(2 * D));
+    const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(V + head, (uint32_t)N * (uint32_t)(2 * D));
+    ld.load(krs, t_lo, N, kbuf0, wave);
+    ld.load(vrs, t_lo, N, vbuf0, wave);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -379,8 +383,8 @@ void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const
         const char* kb = B ? kbuf1 : kbuf0;
         const char* vb = B ? vbuf1 : vbuf0;
         if (u + 1 < n_tiles) {
-            ld.load(K + head, t + 1, N, B ? kbuf0 : kbuf1, wave);
-            ld.load(V + head, t + 1, N, B ? vbuf0 : vbuf1, wave);
+            ld.load(krs, t + 1, N, B ? kbuf0 : kbuf1, wave);
+            ld.load(vrs, t + 1, N, B ? vbuf0 : vbuf1, wave);
         }
         // S^T = K_t Q^T and dP^T = V_t dO^T: rows = the tile's keys, columns = queries (lanes)
         f32x16 st, dpt;

@@ -18,7 +18,7 @@
 // allowed key for one of its rows; tiles wholly outside the mask are never visited
 // and element masking runs only on tiles that straddle the mask or the sequence end.
 //
-// K/V staging.  Each K and V tile goes HBM -> LDS directly (global_load_lds_dwordx4,
+// K/V staging.  Each K and V tile goes HBM -> LDS directly (buffer_load_dwordx4 ... lds,
 // no VGPR round trip), row-major with the 16-byte chunks of a row XOR-swizzled by
 // the row index.  K and V each rotate through two buffers; one barrier per tile.
 // The four buffers are distinct LDS arrays and the tile loop is unrolled by two,
@@ -347,29 +347,30 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         else return t_lo + u;
     };
 
-    // direct HBM -> LDS load of tile t of one tensor into `dst` (this wave's share)
-    auto dma = [&](const __bf16* src, int t, char* dst) __attribute__((always_inline)) {
+    // direct HBM -> LDS load of tile t of one tensor into `dst` (this wave's share):
+    // per-lane offsets fixed for the kernel, the tile's offset a scalar
+    const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(Kh, (uint32_t)Nk * (uint32_t)(D * 2));
+    const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(Vh, (uint32_t)Nk * (uint32_t)(D * 2));
+    auto dma = [&](__amdgpu_buffer_rsrc_t rs, int t, char* dst) __attribute__((always_inline)) {
         const int key0 = t * BC;
-        const char* base = reinterpret_cast<const char*>(src + (size_t)key0 * D);
         if (key0 + BC <= Nk) {
+            const uint32_t soff = (uint32_t)key0 * (uint32_t)(D * 2);
 #pragma unroll
             for (int i = 0; i < C::LOADS_PER_WAVE; ++i)
-                __builtin_amdgcn_global_load_lds((const void*)(base + ld_off[i]),
-                                                 (lds_void*)(dst + (wave * C::LOADS_PER_WAVE + i) * 1024), 16, 0, 0);
+                dma16(rs, (lds_void*)(dst + (wave * C::LOADS_PER_WAVE + i) * 1024), ld_off[i], soff);
         } else {
             // last tile: rows past the end load the last key row (any valid row; masked
             // later).  A tile wholly past the end (the last block of a block layout)
             // has rows_left < 0 and loads that row for every row.
             int kb0 = key0;                                                  // first row read
             if constexpr (BLK) kb0 = min(key0, Nk - 1);     // only block layouts reach past the end
-            const char* tbase = BLK ? reinterpret_cast<const char*>(src + (size_t)kb0 * D) : base;
+            const uint32_t soff = (uint32_t)kb0 * (uint32_t)(D * 2);
             const int rows_left = Nk - 1 - kb0;                              // >= 0
 #pragma unroll
             for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
                 const int row = (int)(ld_off[i] / (2 * D));
                 const uint32_t off = ld_off[i] - (uint32_t)(row - min(row, rows_left)) * (2 * D);
-                __builtin_amdgcn_global_load_lds((const void*)(tbase + off),
-                                                 (lds_void*)(dst + (wave * C::LOADS_PER_WAVE + i) * 1024), 16, 0, 0);
+                dma16(rs, (lds_void*)(dst + (wave * C::LOADS_PER_WAVE + i) * 1024), off, soff);
             }
         }
     };
@@ -632,8 +633,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         for (int k = 0; k < NKS; ++k) { pr[0][b][k] = (bf16x8){}; pr[1][b][k] = (bf16x8){}; }
     for (int i = tid * 16; i < C::TILE_BYTES; i += C::NT * 16)
         *reinterpret_cast<u32x4*>(vbuf1 + i) = (u32x4){0u, 0u, 0u, 0u};
-    dma(Kh, BLK ? tile_of(0) : t_lo, kbuf0);
-    if (n_tiles > 1) dma(Kh, BLK ? tile_of(1) : t_lo + 1, kbuf1);
+    dma(krs, BLK ? tile_of(0) : t_lo, kbuf0);
+    if (n_tiles > 1) dma(krs, BLK ? tile_of(1) : t_lo + 1, kbuf1);
     // Q was requested at kernel start and is waited for only here (the wait orders
     // the pinning below after the tile requests), so the Q loads and the first K
     // tiles are in flight together.  From here on Q sits in AGPRs, written (and
@@ -656,8 +657,8 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         const char* k_next = B ? kbuf0 : kbuf1;           // K(t+1)
         char* v_own = B ? vbuf1 : vbuf0;                  // held V(t-2) (consumed); receives V(t)
         const char* v_prev = B ? vbuf0 : vbuf1;           // V(t-1)
-        if (u + 2 < n_tiles) dma(Kh, BLK ? tile_of(u + 2) : t + 2, k_own);
-        dma(Vh, t, v_own);
+        if (u + 2 < n_tiles) dma(krs, BLK ? tile_of(u + 2) : t + 2, k_own);
+        dma(vrs, t, v_own);
         mask_tile(IntC<B>{}, t);
 
         float mx[QB], alpha[QB], se[QB], sr[QB];

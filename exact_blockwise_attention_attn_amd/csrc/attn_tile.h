@@ -47,6 +47,21 @@ inline int head_group(int N, int d) {
     return 8 * (int)(fit < 1 ? 1 : (fit > (1 << 20) ? (1 << 20) : fit));
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (stride 0; offsets range-checked
+// against `bytes`; word 3 is the gfx9 raw-buffer format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct HBM -> LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds): the
+// bytes at byte offset voff + soff of the buffer land at dst + 16 * lane.  The
+// MUBUF form matters: while a FLAT-encoded direct load (global_load_lds) is in
+// flight the compiler cannot count LDS reads in order and waits for all of them
+// (lgkmcnt(0)) before every use of one; with buffer loads its waits are exact.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_void* dst, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (int)voff, (int)soff, 0, 0);
+}
+
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
     if constexpr (I < N) {

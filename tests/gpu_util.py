@@ -143,7 +143,8 @@ class _forced:
     def __enter__(self):
         self.old = _SCHED[self.key]
         if self.value is not None:
-            _SCHED[self.key] = int(self.value)
+            # "auto": the library's own choice (rows per wave 0, head group -1)
+            _SCHED[self.key] = (0 if self.key == "rows_per_wave" else -1) if self.value == "auto" else int(self.value)
             assert attn.attn_set_schedule(_SCHED["rows_per_wave"], _SCHED["head_group"]) == 0
         return self
 
