@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["attn_api.cpp", "attn_fwd_bf16.hip", "attn_fwd_bf16_d64.hip", "attn_fwd_f32.hip", "attn_bwd_bf16.hip",
-           "attn_decode_bf16.hip"]
+           "attn_decode_bf16.hip", "attn_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

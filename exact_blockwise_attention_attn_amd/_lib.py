@@ -26,6 +26,8 @@ ATTN_ERR_BAD_SCALE = -7
 ATTN_ERR_MISALIGNED = -8
 ATTN_ERR_HIP = -9
 ATTN_ERR_WORKSPACE = -10
+ATTN_ERR_SCRATCH_LIMIT = -11
+ATTN_NOALLOC_SCRATCH_BYTES = 64 << 20
 ATTN_BLOCK_SPARSE_BLOCK = 128
 ATTN_BLOCK_SPARSE_MAX_BLOCKS = 8192
 
@@ -63,6 +65,8 @@ def load():
     lib.attn_fwd_kv.restype = i
     lib.attn_fwd_kv_check_args.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp, u64]
     lib.attn_fwd_kv_check_args.restype = i
+    lib.attn_fwd_kv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, i, vp]
+    lib.attn_fwd_kv_noalloc.restype = i
     lib.attn_fwd_kv_workspace_size.argtypes = [i, i, i, i, i]
     lib.attn_fwd_kv_workspace_size.restype = u64
     lib.attn_fwd_block_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, i, vp]
@@ -105,6 +109,12 @@ def attn_fwd_kv(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_
     """C ``attn_fwd_kv``: pointers as ints, returns the status code."""
     return load().attn_fwd_kv(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_offset, dtype,
                               workspace, workspace_bytes, stream)
+
+
+def attn_fwd_kv_noalloc(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_offset, dtype, stream):
+    """C ``attn_fwd_kv_noalloc``: pointers as ints, returns the status code."""
+    return load().attn_fwd_kv_noalloc(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_offset, dtype,
+                                      stream)
 
 
 def attn_fwd_kv_check_args(q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_offset, dtype, workspace,

@@ -270,6 +270,8 @@ extern "C" const char* attn_strerror(int status) {
         case ATTN_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
         case ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
         case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_fwd_kv_workspace_size()";
+        case ATTN_ERR_SCRATCH_LIMIT:
+            return "attn_fwd_kv_noalloc: the shape needs more scratch than ATTN_NOALLOC_SCRATCH_BYTES (64 MiB)";
         default: return "unknown status";
     }
 }

@@ -51,7 +51,9 @@ enum attn_status {
     ATTN_ERR_BAD_SCALE = -7,             /* scale is NaN or infinite                        */
     ATTN_ERR_MISALIGNED = -8,            /* a tensor pointer is not 16-byte aligned         */
     ATTN_ERR_HIP = -9,                   /* the HIP runtime reported an error at launch     */
-    ATTN_ERR_WORKSPACE = -10             /* workspace NULL or smaller than required         */
+    ATTN_ERR_WORKSPACE = -10,            /* workspace NULL or smaller than required         */
+    ATTN_ERR_SCRATCH_LIMIT = -11         /* attn_fwd_kv_noalloc: the shape needs more than
+                                            ATTN_NOALLOC_SCRATCH_BYTES of scratch           */
 };
 
 /*
@@ -207,6 +209,32 @@ unsigned long long attn_fwd_kv_workspace_size(int B, int H, int Nq, int Nk, int 
 int attn_fwd_kv_check_args(const void* q, const void* k, const void* v, const void* out, const float* lse,
                            int B, int H, int Nq, int Nk, int d, float scale, int mask_kind, int window,
                            int q_offset, int dtype, const void* workspace, unsigned long long workspace_bytes);
+
+/*
+ * attn_fwd_kv_noalloc - attn_fwd_kv for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, kernels and result, with the split-KV
+ * partials kept in a static device array of the library instead of a caller
+ * workspace.  The call allocates and frees nothing.
+ *
+ *   q, k, v, out, lse, B, H, Nq, Nk, d, scale, mask_kind, window, q_offset, dtype,
+ *   stream    as for attn_fwd_kv.
+ *
+ * Limit: shapes whose attn_fwd_kv_workspace_size exceeds ATTN_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) are rejected with ATTN_ERR_SCRATCH_LIMIT before anything is enqueued
+ * (decode fits for any cache size; chunks of Nq queries fit while B * H * splits *
+ * Nq * (d + 1) * 4 bytes does; call attn_fwd_kv with a workspace otherwise).
+ * Each device holds its own copy of the array until the process ends, and every
+ * call on that device shares it: calls whose work may overlap on one device (two
+ * streams, or two host threads) race on it and must be ordered by the caller.  A
+ * call on one stream is safe after any earlier call on the same stream.  Other
+ * errors as for attn_fwd_kv.
+ */
+enum { ATTN_NOALLOC_SCRATCH_BYTES = 67108864 };
+
+int attn_fwd_kv_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int B, int H, int Nq, int Nk, int d, float scale, int mask_kind, int window,
+                        int q_offset, int dtype, void* stream);
 
 /*
  * attn_fwd_block_sparse - exact attention restricted to a block layout.

@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_check_args", "attn_check_args", "attn_fwd",
                                     "attn_fwd_block_sparse", "attn_fwd_block_sparse_check_args", "attn_fwd_kv",
-                                    "attn_fwd_kv_check_args", "attn_fwd_kv_workspace_size", "attn_set_schedule",
+                                    "attn_fwd_kv_check_args", "attn_fwd_kv_noalloc", "attn_fwd_kv_workspace_size", "attn_set_schedule",
                                     "attn_strerror", "attn_version"]
 
 
@@ -41,7 +41,7 @@ def test_header_enums_match_binding():
 
 def test_version_and_strerror():
     assert "gfx950" in attn.attn_version()
-    for code in range(-10, 1):
+    for code in range(-11, 1):
         msg = attn.attn_strerror(code)
         assert msg and msg != "unknown status"
     assert attn.attn_strerror(-100) == "unknown status"
@@ -286,3 +286,11 @@ def test_set_schedule_validates():
         assert attn.attn_set_schedule(rpw, hg) == _lib.ATTN_ERR_BAD_SHAPE
     assert attn.attn_set_schedule(0, -1) == 0
 
+
+def test_noalloc_rejects_over_limit_on_the_host():
+    # a shape whose split-KV partials exceed the static scratch: rejected before any device call
+    B, H, Nq, Nk, d = 1, 255, 256, 512, 128
+    assert attn.attn_fwd_kv_workspace_size(B, H, Nq, Nk, d) > _lib.ATTN_NOALLOC_SCRATCH_BYTES
+    q, k, v, o, l = ptrs()
+    assert attn.attn_fwd_kv_noalloc(q, k, v, o, l, B, H, Nq, Nk, d, 0.1, 1, 0, Nk - Nq, 1, None) == \
+        _lib.ATTN_ERR_SCRATCH_LIMIT
