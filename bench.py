@@ -39,7 +39,12 @@ METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, d=128 N=8192 causal"
 METRIC_BWD = "attention bwd TFLOP/s (2.5x forward FLOPs) and % of bf16 MFMA peak"
 METRIC_DECODE = "attention decode (split-KV) GB/s of K/V cache read and % of HBM peak"
 METRIC_SPARSE = "block-sparse attention fwd TFLOP/s on allowed pairs and % of bf16 MFMA peak"
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}      # MI355X dense bf16 MFMA; fp32 vector
+# MI355X peaks: dense bf16 MFMA 2.5 PFLOP/s.  The fp32 path runs on the vector ALUs
+# (fp32 FMAs and fp64 scores) with packed fp32 instructions disabled in the build, so
+# its ceiling is the unpacked vector rate: 256 CUs x 4 SIMDs x 16 lanes x 2 flop x
+# 2.4 GHz = 78.6 TFLOP/s (the same as the fp64 vector rate).  The 157.3 TFLOP/s fp32
+# figure needs packed issue or fp32 MFMA, neither of which this path uses.
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 78.6}
 HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = "exact_blockwise_attention_attn_amd/csrc/"
@@ -50,6 +55,7 @@ KERNEL_SOURCES = {
     "fwd": [CSRC + "attn_fwd_bf16.hip", CSRC + "attn_fwd_bf16_d64.hip", CSRC + "attn_tile.h", BUILD],
     "decode": [CSRC + "attn_decode_bf16.hip", CSRC + "attn_fwd_bf16.hip", BUILD],
     "bwd": [CSRC + "attn_bwd_bf16.hip", CSRC + "attn_tile.h", BUILD],
+    "f32": [CSRC + "attn_fwd_f32.hip", BUILD],
 }
 
 
@@ -67,6 +73,15 @@ def counted_flops(B, H, N, d, mask, window=0):
 def algorithmic_bytes(B, H, N, d, eb):
     """Read Q, K, V once, write O once and LSE once."""
     return 4 * B * H * N * d * eb + 4 * B * H * N
+
+
+def roofline_bound(flops, nbytes, dtype):
+    """The roof a workload sits under: its arithmetic intensity (counted flops per
+    algorithmic byte) against the ridge point of the unit that does its arithmetic
+    (peak flop rate / HBM peak).  Below the ridge the bound is HBM bandwidth."""
+    unit = "mfma" if dtype == "bf16" else "alu"
+    ridge = PEAK_TFLOPS[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    return (unit if flops / nbytes >= ridge else "hbm"), flops / nbytes, ridge
 
 
 def _code_only(text):
@@ -104,6 +119,25 @@ def measured_traffic(workload, kind="fwd"):
     if not ent or ent.get("source_hash") != kernel_source_hash(kind):
         return None
     return ent.get("bytes_per_launch")
+
+
+class cpu_threads:
+    """Limit the BLAS threads of the oracle baseline to n (n <= 0: leave them)."""
+
+    def __init__(self, n):
+        self.n, self.ctx = n, None
+
+    def __enter__(self):
+        if self.n > 0:
+            from threadpoolctl import threadpool_limits
+            self.ctx = threadpool_limits(limits=self.n)
+            self.ctx.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            self.ctx.__exit__(*exc)
+        return False
 
 
 def cpu_baseline(wl, q, k, v, budget_s=20.0):
@@ -385,6 +419,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="BLAS threads for the oracle baseline (0: every core the process may use; 1 gives the "
+                         "per-core figure)")
     ap.add_argument("--cold", action="store_true",
                     help="write a 512 MiB scratch buffer between steps so every step starts with cold L2/MALL "
                          "(steps are then timed one by one, the flush outside each)")
@@ -493,7 +530,23 @@ def main():
 
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
-    traffic = measured_traffic(name, "fwd") if args.which == "fwd" else measured_traffic(name + "/bwd", "bwd")
+    if args.which == "fwd":
+        traffic = measured_traffic(name, "fwd" if wl.dtype == "bf16" else "f32")
+    else:
+        traffic = measured_traffic(name + "/bwd", "bwd")
+    alg = algorithmic_bytes(wl.B, wl.H, wl.N, wl.d, eb) if args.which == "fwd" else \
+        (5 * wl.B * wl.H * wl.N * wl.d * eb + 3 * wl.B * wl.H * wl.N * wl.d * eb + 4 * wl.B * wl.H * wl.N)
+    bound, intensity, ridge = roofline_bound(flops, alg, wl.dtype)
+    secs = ms_per_step * 1e-3
+    if bound == "hbm":
+        roof = {"bound": "hbm", "achieved": round(alg / secs / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(alg / secs / 1e9 / HBM_PEAK_GBS, 4), "traffic": traffic}
+    else:
+        roof = {"bound": bound, "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(tflops / peak, 4), "traffic": traffic}
+    roof.update({"algorithmic_bytes": alg, "algorithmic_gbs": round(alg / secs / 1e9, 1),
+                 "traffic_gbs": round(traffic / secs / 1e9, 1) if traffic else None,
+                 "flop_per_byte": round(intensity, 1), "ridge_flop_per_byte": round(ridge, 1)})
     rec = {
         "metric": METRIC if args.which == "fwd" else METRIC_BWD,
         "value": round(tflops, 2),
@@ -513,19 +566,15 @@ def main():
                    "ms_median": round(ms_median, 5), "ms_min": round(ms_min, 5),
                    "tflops_at_median": round(flops / (ms_median * 1e-3) / 1e12, 2),
                    "cold_l2": bool(args.cold), "wall_s_timed_region": round(wall, 4)},
-        "roofline": {"bound": "mfma" if wl.dtype == "bf16" else "alu", "achieved": round(tflops, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": traffic,
-                     "algorithmic_bytes": algorithmic_bytes(wl.B, wl.H, wl.N, wl.d, eb),
-                     "algorithmic_gbs": round(algorithmic_bytes(wl.B, wl.H, wl.N, wl.d, eb)
-                                              / (ms_per_step * 1e-3) / 1e9, 1)},
+        "roofline": roof,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        if args.which == "fwd":
-            rec["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget)
-        else:
-            rec["cpu_baseline"] = cpu_baseline_bwd(wl, q, k, v, dout, args.cpu_budget)
+        with cpu_threads(args.cpu_threads):
+            if args.which == "fwd":
+                rec["cpu_baseline"] = cpu_baseline(wl, q, k, v, args.cpu_budget)
+            else:
+                rec["cpu_baseline"] = cpu_baseline_bwd(wl, q, k, v, dout, args.cpu_budget)
     print(json.dumps(rec), flush=True)
 
 
