@@ -75,6 +75,8 @@ def load():
     lib.attn_fwd_block_sparse_check_args.restype = i
     lib.attn_set_schedule.argtypes = [i, i]
     lib.attn_set_schedule.restype = i
+    lib.attn_set_key_groups.argtypes = [i]
+    lib.attn_set_key_groups.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -144,6 +146,13 @@ def attn_set_schedule(rows_per_wave: int, head_group: int) -> int:
     the library's choice) and head-group size (n, 0 = one group, -1 = the library's
     choice) for later calls; returns the status code."""
     return load().attn_set_schedule(rows_per_wave, head_group)
+
+
+def attn_set_key_groups(key_groups: int) -> int:
+    """C ``attn_set_key_groups``: force 1, 2 or 4 key groups in the bf16 forward
+    with no mask or the causal mask (-1 = the library's choice) for later calls;
+    returns the status code."""
+    return load().attn_set_key_groups(key_groups)
 
 
 def attn_strerror(status: int) -> str:

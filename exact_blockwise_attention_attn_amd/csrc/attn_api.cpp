@@ -246,14 +246,23 @@ extern "C" int attn_fwd_block_sparse(const void* q, const void* k, const void* v
 static std::atomic<int> g_rows_per_wave{0};
 static std::atomic<int> g_head_group{-1};
 
+static std::atomic<int> g_key_groups{-1};
+
 int attn_sched_rows_per_wave() { return g_rows_per_wave.load(std::memory_order_relaxed); }
 int attn_sched_head_group() { return g_head_group.load(std::memory_order_relaxed); }
+int attn_sched_key_groups() { return g_key_groups.load(std::memory_order_relaxed); }
 
 extern "C" int attn_set_schedule(int rows_per_wave, int head_group) {
     if (rows_per_wave != 0 && rows_per_wave != 32 && rows_per_wave != 64) return ATTN_ERR_BAD_SHAPE;
     if (head_group < -1) return ATTN_ERR_BAD_SHAPE;
     g_rows_per_wave.store(rows_per_wave, std::memory_order_relaxed);
     g_head_group.store(head_group, std::memory_order_relaxed);
+    return ATTN_OK;
+}
+
+extern "C" int attn_set_key_groups(int key_groups) {
+    if (key_groups != -1 && key_groups != 1 && key_groups != 2 && key_groups != 4) return ATTN_ERR_BAD_SHAPE;
+    g_key_groups.store(key_groups, std::memory_order_relaxed);
     return ATTN_OK;
 }
 

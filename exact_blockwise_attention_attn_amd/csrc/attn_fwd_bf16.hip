@@ -17,6 +17,12 @@
 // (grouped_order).  The workgroup walks the key tiles (BC = 32 keys) that hold an
 // allowed key for one of its rows; tiles wholly outside the mask are never visited
 // and element masking runs only on tiles that straddle the mask or the sequence end.
+// A grid too small for the device (no mask or causal) splits the keys as well: the
+// four waves form 4 / KG sets of query rows times KG key groups, group j takes tiles
+// t_lo + KG u + j, and the groups' softmax states are merged through LDS at the end
+// with weights 2^(m_j - max m), the exact combination of softmax pieces over disjoint
+// key sets (the Mosaic page's merge of local attention results, §2.1, of the blocks
+// of its §2.2).  KG = 2 or 4 doubles or quadruples the workgroups of a shape.
 //
 // K/V staging.  Each K and V tile goes HBM -> LDS directly (buffer_load_dwordx4 ... lds,
 // no VGPR round trip), row-major with the 16-byte chunks of a row XOR-swizzled by
@@ -73,19 +79,24 @@ constexpr float TAU = 8.0f;         // lazy rescale threshold (log2 domain)
 
 // Tile shape: a wave owns QB blocks of 32 query rows; a key tile is KB blocks of
 // 32 keys.  Each K or V operand read from LDS feeds QB matrix instructions.
-template <int D, int QB, int KB>
+// KG key groups: the waves of a workgroup form NW / KG row groups (distinct query
+// rows) times KG key groups; at step u key group g takes tile t_lo + KG u + g, and
+// the groups' softmax states are merged at the end (exact, as for disjoint key sets).
+template <int D, int QB, int KB, int KG = 1>
 struct Cfg {
     static constexpr int NW = 4;                    // waves per workgroup, one per SIMD
+    static constexpr int RG = NW / KG;              // row groups
     static constexpr int RW = 32 * QB;              // query rows per wave
     static constexpr int BC = 32 * KB;              // keys per tile
     static constexpr int NT = 64 * NW;              // threads per workgroup
-    static constexpr int BR = RW * NW;              // query rows per workgroup
+    static constexpr int BR = RW * RG;              // query rows per workgroup
     static constexpr int TILE_BYTES = BC * D * 2;   // one K or V tile
-    static constexpr int LDS_BYTES = 4 * TILE_BYTES;             // K and V, two buffers each
-    static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / NW;  // 1 KB per wave instruction
+    static constexpr int LDS_BYTES = 4 * KG * TILE_BYTES;        // K and V, two buffers each, per key group
+    static constexpr int LOADS_PER_WAVE = TILE_BYTES / 1024 / RG;  // a key group's waves load its tile, 1 KB per instruction
     static constexpr int RB = BC / 16;              // 16-row blocks of a tile (one 1 KB load each per chunk group)
+    static_assert(KG == 1 || KG == 2 || KG == 4, "key groups");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one CDNA4 workgroup");
-    static_assert(TILE_BYTES % (1024 * NW) == 0, "tile must split evenly over the waves");
+    static_assert(TILE_BYTES % (1024 * RG) == 0, "tile must split evenly over the waves");
     static_assert(D == 64 || D == 128, "head dim");
 };
 
@@ -166,31 +177,35 @@ struct BlockArgs {
     int nb;                  // ceil(N / BLOCK_TOKENS)
 };
 
-template <int D, int QB, int MASK, bool SPLIT>
+template <int D, int QB, int MASK, bool SPLIT, int KG>
 constexpr int min_waves_per_simd() {
-    return (D == 128 && QB == 1) ? 2 : 1;
+    return ((D == 128 && QB == 1) || (D == 64 && QB == 1 && KG > 1)) ? 2 : 1;
 }
 
-template <int D, int QB, int KB, int MASK, bool SPLIT = false>
+template <int D, int QB, int KB, int MASK, bool SPLIT = false, int KG = 1>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
-                          amdgpu_waves_per_eu(min_waves_per_simd<D, QB, MASK, SPLIT>(), 8)))
+                          amdgpu_waves_per_eu(min_waves_per_simd<D, QB, MASK, SPLIT, KG>(), 8)))
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                 const __bf16* __restrict__ V, __bf16* __restrict__ O, float* __restrict__ LSE,
                 int BH, int N, int nqt, float c_log2, int negate_q, int window, SplitArgs sa = SplitArgs{},
                 BlockArgs ba = BlockArgs{}, int hg = 0) {
-    using C = Cfg<D, QB, KB>;
+    using C = Cfg<D, QB, KB, KG>;
     constexpr int BC = C::BC;
     constexpr int NS = D / 16;       // 16-dim slabs of the contraction over d
     constexpr int ND = D / 32;       // 32-row blocks of O^T
     constexpr int NKS = BC / 16;     // 16-key slabs of the V product
-    // K and V tiles rotate through two buffers each; four distinct arrays
-    __shared__ __attribute__((aligned(1024))) char kbuf0[C::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char kbuf1[C::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char vbuf0[C::TILE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char vbuf1[C::TILE_BYTES];
+    // K and V tiles rotate through two buffers each; four distinct arrays, each with
+    // one tile per key group
+    __shared__ __attribute__((aligned(1024))) char kbuf0[KG * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char kbuf1[KG * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char vbuf0[KG * C::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char vbuf1[KG * C::TILE_BYTES];
     constexpr bool BLK = (MASK == MASK_BLOCK || MASK == MASK_BLOCK_CAUSAL);
     constexpr bool CAUS = (MASK == ATTN_MASK_CAUSAL || MASK == MASK_BLOCK_CAUSAL);
     static_assert(!BLK || (QB == 1 && KB == 1 && !SPLIT), "block layouts use 128-row query blocks of 32-key tiles");
+    static_assert(KG == 1 || (!BLK && !SPLIT), "key groups: dense masks of the full forward");
+    // merge of the key groups: per-lane scalars (running max, both sums) of groups 1..KG-1
+    __shared__ float mstate[KG > 1 ? (KG - 1) * C::RG * QB * 3 * 64 : 1];
     __shared__ uint16_t blist[BLK ? MAX_LAYOUT_BLOCKS : 1];   // allowed key blocks of this query block
     __shared__ int bcount;
 
@@ -199,6 +214,13 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hl = lane >> 5;        // lane half
     const int ln = lane & 31;
+    const int kg = KG == 1 ? 0 : wave / C::RG;    // key group
+    const int rg = KG == 1 ? wave : wave % C::RG; // row group
+    // this key group's tile in each buffer
+    char* const kb0 = kbuf0 + kg * C::TILE_BYTES;
+    char* const kb1 = kbuf1 + kg * C::TILE_BYTES;
+    char* const vb0 = vbuf0 + kg * C::TILE_BYTES;
+    char* const vb1 = vbuf1 + kg * C::TILE_BYTES;
 
     // Workgroup order: heads in groups of hg (grouped_order), inside a group the
     // heaviest query blocks first for the causal mask.
@@ -238,7 +260,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     const __bf16* Kh = K + khead;
     const __bf16* Vh = V + khead;
 
-    const int qw0 = q0 + wave * C::RW;           // first row of this wave
+    const int qw0 = q0 + rg * C::RW;             // first row of this wave
     int my_q[QB];                                // the query of this lane's column in each 32-row block
 #pragma unroll
     for (int b = 0; b < QB; ++b) my_q[b] = qw0 + 32 * b + ln;
@@ -254,12 +276,12 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             qreg[b][s] = __builtin_bit_cast(bf16x8, raw);
         }
     // ---- per-lane LDS and load addresses (byte offsets within a tile)
-    // loader: wave instruction i fills 1 KB block b = wave * LPW + i, i.e. rows
+    // loader: wave instruction i fills 1 KB block b = rg * LPW + i, i.e. rows
     // 16 (b % RB) .. +15 of chunk group b / RB; lane -> (row, chunk)
     uint32_t ld_off[C::LOADS_PER_WAVE];          // byte offset of the lane's 16 bytes in the HBM tile
 #pragma unroll
     for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
-        const int b = wave * C::LOADS_PER_WAVE + i;
+        const int b = rg * C::LOADS_PER_WAVE + i;
         const int row = 16 * (b % C::RB) + (lane >> 2);
         const int c = 4 * (b / C::RB) + ((lane & 3) ^ ((row >> 2) & 3));
         ld_off[i] = (uint32_t)(row * D + c * 8) * 2u;
@@ -340,11 +362,19 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         }
     }
     const int n_tiles = t_hi - t_lo + 1;
-    // key tile of step u: the range's u-th tile, or the u-th tile of the allowed blocks
-    // (a block's tiles past the sequence end load the last key row and are masked)
+    const int n_steps = KG == 1 ? n_tiles : (n_tiles + KG - 1) / KG;
+    // key tile of step u: the range's u-th tile (tile KG u + kg with key groups), or
+    // the u-th tile of the allowed blocks (a block's tiles past the sequence end load
+    // the last key row and are masked).  A key group's tile past t_hi (the last step
+    // of a range that does not split evenly) holds no allowed key of the workgroup's
+    // rows: it is masked out whole, and the last tile of the range is loaded for it.
     auto tile_of = [&](int u) __attribute__((always_inline)) -> int {
         if constexpr (BLK) return __builtin_amdgcn_readfirstlane(4 * (int)blist[u >> 2] + (u & 3));
-        else return t_lo + u;
+        else return t_lo + KG * u + kg;
+    };
+    auto tile_ld = [&](int u) __attribute__((always_inline)) -> int {
+        if constexpr (KG > 1) return min(tile_of(u), t_hi);
+        else return tile_of(u);
     };
 
     // direct HBM -> LDS load of tile t of one tensor into `dst` (this wave's share):
@@ -357,7 +387,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             const uint32_t soff = (uint32_t)key0 * (uint32_t)(D * 2);
 #pragma unroll
             for (int i = 0; i < C::LOADS_PER_WAVE; ++i)
-                dma16(rs, (lds_void*)(dst + (wave * C::LOADS_PER_WAVE + i) * 1024), ld_off[i], soff);
+                dma16(rs, (lds_void*)(dst + (rg * C::LOADS_PER_WAVE + i) * 1024), ld_off[i], soff);
         } else {
             // last tile: rows past the end load the last key row (any valid row; masked
             // later).  A tile wholly past the end (the last block of a block layout)
@@ -370,7 +400,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             for (int i = 0; i < C::LOADS_PER_WAVE; ++i) {
                 const int row = (int)(ld_off[i] / (2 * D));
                 const uint32_t off = ld_off[i] - (uint32_t)(row - min(row, rows_left)) * (2 * D);
-                dma16(rs, (lds_void*)(dst + (wave * C::LOADS_PER_WAVE + i) * 1024), off, soff);
+                dma16(rs, (lds_void*)(dst + (rg * C::LOADS_PER_WAVE + i) * 1024), off, soff);
             }
         }
     };
@@ -631,10 +661,10 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     for (int b = 0; b < QB; ++b)
 #pragma unroll
         for (int k = 0; k < NKS; ++k) { pr[0][b][k] = (bf16x8){}; pr[1][b][k] = (bf16x8){}; }
-    for (int i = tid * 16; i < C::TILE_BYTES; i += C::NT * 16)
+    for (int i = tid * 16; i < KG * C::TILE_BYTES; i += C::NT * 16)
         *reinterpret_cast<u32x4*>(vbuf1 + i) = (u32x4){0u, 0u, 0u, 0u};
-    dma(krs, BLK ? tile_of(0) : t_lo, kbuf0);
-    if (n_tiles > 1) dma(krs, BLK ? tile_of(1) : t_lo + 1, kbuf1);
+    dma(krs, tile_ld(0), kb0);
+    if (n_steps > 1) dma(krs, tile_ld(1), kb1);
     // Q was requested at kernel start and is waited for only here (the wait orders
     // the pinning below after the tile requests), so the Q loads and the first K
     // tiles are in flight together.  From here on Q sits in AGPRs, written (and
@@ -645,7 +675,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int s = 0; s < NS; ++s) settle_qa(qreg[b][s]);
     __syncthreads();
-    scores(IntC<0>{}, kbuf0);
+    scores(IntC<0>{}, kb0);
     settle_scores(IntC<0>{});
     __syncthreads();     // every wave is done with K(t_lo) before tile 0 refills its buffer
 
@@ -653,12 +683,12 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         constexpr int B = decltype(parity)::value;        // u % 2
         constexpr int X = 1 - B;
         const int t = tile_of(u);
-        char* k_own = B ? kbuf1 : kbuf0;                  // held K(t) (consumed); receives K(t+2)
-        const char* k_next = B ? kbuf0 : kbuf1;           // K(t+1)
-        char* v_own = B ? vbuf1 : vbuf0;                  // held V(t-2) (consumed); receives V(t)
-        const char* v_prev = B ? vbuf0 : vbuf1;           // V(t-1)
-        if (u + 2 < n_tiles) dma(krs, BLK ? tile_of(u + 2) : t + 2, k_own);
-        dma(vrs, t, v_own);
+        char* k_own = B ? kb1 : kb0;                      // held K(t) (consumed); receives K of step u+2
+        const char* k_next = B ? kb0 : kb1;               // K of step u+1
+        char* v_own = B ? vb1 : vb0;                      // held V of step u-2 (consumed); receives V(t)
+        const char* v_prev = B ? vb0 : vb1;               // V of step u-1
+        if (u + 2 < n_steps) dma(krs, tile_ld(u + 2), k_own);
+        dma(vrs, KG > 1 ? tile_ld(u) : t, v_own);
         mask_tile(IntC<B>{}, t);
 
         float mx[QB], alpha[QB], se[QB], sr[QB];
@@ -718,13 +748,95 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         __syncthreads();
     };
     int u = 0;
-    for (; u + 1 < n_tiles; u += 2) {
+    for (; u + 1 < n_steps; u += 2) {
         iter(IntC<0>{}, u);
         iter(IntC<1>{}, u + 1);
     }
-    if (u < n_tiles) iter(IntC<0>{}, u++);
-    // closing step: the V product of the last tile (V(n_tiles - 1) in vbuf[(n_tiles - 1) % 2])
-    if (u & 1) pv(IntC<0>{}, vbuf0); else pv(IntC<1>{}, vbuf1);
+    if (u < n_steps) iter(IntC<0>{}, u++);
+    // closing step: the V product of the last step (its V in vbuf[(n_steps - 1) % 2])
+    if (u & 1) pv(IntC<0>{}, vb0); else pv(IntC<1>{}, vb1);
+
+    // ---- key groups: merge the softmax states of groups 1 .. KG-1 into group 0.  With
+    // M = max over groups of the running maximum m_g and weight a_g = 2^(m_g - M) (0
+    // for a group that met no allowed key of the row), O = sum a_g O_g, and both sums
+    // likewise: the combination of softmax pieces over disjoint key sets.  Group g's
+    // accumulators go through the (idle) tile buffers, lane by lane in the layout
+    // both waves share.
+    if constexpr (KG > 1) {
+        // one piece per (group g >= 1, row group, 32-row block b): ND x 4 x 64 lanes x 16 bytes,
+        // KG / 2 pieces per buffer
+        constexpr int PIECE = ND * 4 * 64 * 16;
+        constexpr int PPB = KG / 2;
+        static_assert(PPB * PIECE <= KG * C::TILE_BYTES, "pieces fit a buffer");
+        static_assert((KG - 1) * C::RG * QB <= 4 * PPB, "merge fits the tile buffers");
+        __syncthreads();                 // every wave is done with the tile buffers
+        auto o_slot = [&](int g, int b, int j, int q) __attribute__((always_inline)) -> float4* {
+            // quarter q of 32-row block j of O^T; lanes contiguous
+            const int piece = ((g - 1) * C::RG + rg) * QB + b;
+            const int k = piece / PPB;
+            char* const buf = k == 0 ? kbuf0 : k == 1 ? kbuf1 : k == 2 ? vbuf0 : vbuf1;
+            return reinterpret_cast<float4*>(buf + (piece % PPB) * PIECE) + (j * 4 + q) * 64 + lane;
+        };
+        auto s_slot = [&](int g, int b, int k) __attribute__((always_inline)) -> float* {
+            return mstate + ((((g - 1) * C::RG + rg) * QB + b) * 3 + k) * 64 + lane;
+        };
+        if (kg > 0) {
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+#pragma unroll
+                for (int j = 0; j < ND; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *o_slot(kg, b, j, q) = make_float4(o[b][j][4 * q], o[b][j][4 * q + 1], o[b][j][4 * q + 2], o[b][j][4 * q + 3]);
+                *s_slot(kg, b, 0) = m_run[b];
+                *s_slot(kg, b, 1) = l_exp[b];
+                *s_slot(kg, b, 2) = RSM ? lr_acc[b][0] : l_rnd[b];
+            }
+        }
+        __syncthreads();
+        if (kg == 0) {
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                float mg[KG];
+                mg[0] = m_run[b];
+#pragma unroll
+                for (int g = 1; g < KG; ++g) mg[g] = *s_slot(g, b, 0);
+                float M = mg[0];
+#pragma unroll
+                for (int g = 1; g < KG; ++g) M = fmaxf(M, mg[g]);
+                float a[KG];
+#pragma unroll
+                for (int g = 0; g < KG; ++g) a[g] = mg[g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mg[g] - M);
+                float le = a[0] * l_exp[b], lr = a[0] * (RSM ? lr_acc[b][0] : l_rnd[b]);
+#pragma unroll
+                for (int g = 1; g < KG; ++g) {
+                    le = __builtin_fmaf(a[g], *s_slot(g, b, 1), le);
+                    lr = __builtin_fmaf(a[g], *s_slot(g, b, 2), lr);
+                }
+#pragma unroll
+                for (int j = 0; j < ND; ++j) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[b][j][r] *= a[0];
+#pragma unroll
+                    for (int g = 1; g < KG; ++g)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float4 x = *o_slot(g, b, j, q);
+                            o[b][j][4 * q] = __builtin_fmaf(a[g], x.x, o[b][j][4 * q]);
+                            o[b][j][4 * q + 1] = __builtin_fmaf(a[g], x.y, o[b][j][4 * q + 1]);
+                            o[b][j][4 * q + 2] = __builtin_fmaf(a[g], x.z, o[b][j][4 * q + 2]);
+                            o[b][j][4 * q + 3] = __builtin_fmaf(a[g], x.w, o[b][j][4 * q + 3]);
+                        }
+                }
+                m_run[b] = M;
+                l_exp[b] = le;
+                if constexpr (RSM) lr_acc[b][0] = lr;
+                else l_rnd[b] = lr;
+            }
+        }
+        __syncthreads();                 // the merge reads are done before the staging writes
+        if (kg > 0) return;              // no barrier follows
+    }
 
     // ---- epilogue: O = acc / sum bf16(p) (bf16, nearest even), LSE = (m + log2 sum p) ln 2
     // A lane holds 16 values of one O row, so direct stores would write 16-byte
@@ -732,7 +844,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // one of the (now idle) tile buffers, row-major with the 16-byte chunks rotated
     // by the row (no bank conflicts), and writes whole rows: 1 KB per instruction.
     const bool partials = SPLIT && sa.n_split > 1;
-    if (!partials) __syncthreads();      // every wave is done with the tile buffers
+    if (!partials && KG == 1) __syncthreads();      // every wave is done with the tile buffers
     char* const stage = wave == 0 ? kbuf0 : wave == 1 ? kbuf1 : wave == 2 ? vbuf0 : vbuf1;
     constexpr int ROWB = 2 * D;          // bytes of one bf16 O row
     constexpr int NCH = D / 8;           // 16-byte chunks per row
@@ -791,14 +903,14 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     }
 }
 
-template <int D, int QB, int KB, int MASK>
+template <int D, int QB, int KB, int MASK, int KG = 1>
 static int launch(const AttnLaunch& a) {
-    using C = Cfg<D, QB, KB>;
+    using C = Cfg<D, QB, KB, KG>;
     const int nqt = (a.N + C::BR - 1) / C::BR;
     const long long grid = (long long)nqt * a.B * a.H;
     int hg = attn_sched_head_group();
     if (hg < 0) hg = head_group(a.N, a.d);      // K and V of a head: causal B4 H32 N16384 d128 +12%
-    hipLaunchKernelGGL((fwd_kernel<D, QB, KB, MASK>), dim3((unsigned)grid), dim3(C::NT), 0, (hipStream_t)a.stream,
+    hipLaunchKernelGGL((fwd_kernel<D, QB, KB, MASK, false, KG>), dim3((unsigned)grid), dim3(C::NT), 0, (hipStream_t)a.stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v, (__bf16*)a.out, a.lse,
                        a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window, SplitArgs{}, BlockArgs{}, hg);
     return 0;
@@ -883,13 +995,33 @@ static int by_mask_split(const AttnLaunch& a, const SplitArgs& sa) {
     }
 }
 
-template <int D, int QB, int KB>
+template <int D, int QB, int KB, int KG = 1>
 static int by_mask(const AttnLaunch& a) {
     switch (a.mask_kind) {
-        case ATTN_MASK_CAUSAL: return launch<D, QB, KB, ATTN_MASK_CAUSAL>(a);
-        case ATTN_MASK_WINDOW: return launch<D, QB, KB, ATTN_MASK_WINDOW>(a);
-        case ATTN_MASK_CAUSAL_WINDOW: return launch<D, QB, KB, ATTN_MASK_CAUSAL_WINDOW>(a);
-        default: return launch<D, QB, KB, ATTN_MASK_NONE>(a);
+        case ATTN_MASK_CAUSAL: return launch<D, QB, KB, ATTN_MASK_CAUSAL, KG>(a);
+        case ATTN_MASK_WINDOW: return launch<D, QB, KB, ATTN_MASK_WINDOW, KG>(a);
+        case ATTN_MASK_CAUSAL_WINDOW: return launch<D, QB, KB, ATTN_MASK_CAUSAL_WINDOW, KG>(a);
+        default: return launch<D, QB, KB, ATTN_MASK_NONE, KG>(a);
+    }
+}
+
+// key groups: the dense masks only (no mask, causal)
+template <int D, int QB, int KG>
+static int by_mask_kg(const AttnLaunch& a) {
+    switch (a.mask_kind) {
+        case ATTN_MASK_CAUSAL: return launch<D, QB, 1, ATTN_MASK_CAUSAL, KG>(a);
+        case ATTN_MASK_NONE: return launch<D, QB, 1, ATTN_MASK_NONE, KG>(a);
+        default: return ATTN_ERR_BAD_MASK;      // never chosen for the band masks
+    }
+}
+
+// the kernel of one tile shape: 32 or 64 query rows per wave, 1, 2 or 4 key groups
+template <int D>
+static int by_shape(const AttnLaunch& a, bool rows32, int key_groups) {
+    switch (key_groups) {
+        case 2: return rows32 ? by_mask_kg<D, 1, 2>(a) : by_mask_kg<D, 2, 2>(a);
+        case 4: return rows32 ? by_mask_kg<D, 1, 4>(a) : by_mask_kg<D, 2, 4>(a);
+        default: return rows32 ? by_mask<D, 1, 1>(a) : by_mask<D, 2, 1>(a);
     }
 }
 
@@ -898,9 +1030,9 @@ static int by_mask(const AttnLaunch& a) {
 #ifdef ATTN_FWD_D64_TU
 // The dense d = 64 kernels, compiled in a translation unit of their own
 // (attn_fwd_bf16_d64.hip) with matrix-instruction accumulators in VGPRs.
-int attn_launch_bf16_d64(const AttnLaunch& a, bool rows32) {
+int attn_launch_bf16_d64(const AttnLaunch& a, bool rows32, int key_groups) {
     using namespace attn_bf16;
-    return rows32 ? by_mask<64, 1, 1>(a) : by_mask<64, 2, 1>(a);
+    return by_shape<64>(a, rows32, key_groups);
 }
 #else
 
@@ -935,11 +1067,48 @@ int attn_launch_bf16(const AttnLaunch& a) {
                                (a.mask_kind == ATTN_MASK_CAUSAL_WINDOW && a.window >= a.N - 1)) &&
                               a.N < (a.d == 64 ? 16384 : 8192);
     bool rows32 = band || short_causal || grid64 < 2LL * device_cus();
-    // explicit choice (both variants compute the same result; tests run each)
-    const int forced = attn_sched_rows_per_wave();
-    if (forced) rows32 = forced == 32;
-    if (a.d == 128) return rows32 ? by_mask<128, 1, 1>(a) : by_mask<128, 2, 1>(a);
-    return attn_launch_bf16_d64(a, rows32);
+
+    // Key groups (no mask or causal) where the query blocks alone leave the device
+    // short of work; g32 = workgroups of 128 query rows, c = compute units.  From A/B
+    // timing of every shape on one MI355X (TFLOP/s, one key group -> the choice):
+    //   d = 128: g32 <= c, or causal g32 <= 2c: 64 rows x 2 groups (H8 N4096 898 -> 962,
+    //            causal H8 N8192 802 -> 948, causal H4 N16384 821 -> 1002);
+    //   d = 64:  g32 <= c / 2, or causal g32 <= c: 64 rows x 4 groups (H4 N4096 319 -> 564,
+    //            causal H4 N8192 328 -> 552); g32 <= c, or causal g32 <= 2c: 32 rows x
+    //            2 groups (H8 N4096 584 -> 694, causal H8 N8192 605 -> 769).
+    // Above that one group wins (H16 N4096 d64 840 against 757).
+    const bool dense = a.mask_kind == ATTN_MASK_NONE || a.mask_kind == ATTN_MASK_CAUSAL;
+    bool plan_rows32 = false;
+    int plan_kg = 1;
+    if (dense) {
+        const bool causal = a.mask_kind == ATTN_MASK_CAUSAL;
+        const long long c = device_cus();
+        const long long g32 = (long long)((a.N + 127) / 128) * a.B * a.H;
+        if (a.d == 128) {
+            if (g32 <= (causal ? 2 * c : c)) plan_kg = 2;
+        } else if (g32 <= (causal ? c : c / 2)) {
+            plan_kg = 4;
+        } else if (g32 <= (causal ? 2 * c : c)) {
+            plan_kg = 2;
+            plan_rows32 = true;
+        }
+    }
+    // explicit choices (every choice computes the same attention; tests run each)
+    const int forced_rows = attn_sched_rows_per_wave();
+    const int forced_kg = attn_sched_key_groups();
+    int kg = 1;
+    if (forced_kg > 0) {
+        kg = dense ? forced_kg : 1;
+        if (forced_rows) rows32 = forced_rows == 32;
+        else if (kg > 1) rows32 = a.d == 64 && kg == 2;
+    } else if (plan_kg > 1 && (!forced_rows || (forced_rows == 32) == plan_rows32)) {
+        kg = plan_kg;
+        rows32 = plan_rows32;
+    } else if (forced_rows) {
+        rows32 = forced_rows == 32;
+    }
+    if (a.d == 128) return by_shape<128>(a, rows32, kg);
+    return attn_launch_bf16_d64(a, rows32, kg);
 }
 
 // Key ranges for the split-KV path: enough workgroups to fill the 256 CUs twice, at

@@ -38,12 +38,14 @@ struct AttnBwdLaunch {
     void* stream;
 };
 
-// Schedule overrides set through attn_set_schedule (0 / -1: the library's choice).
+// Schedule overrides set through attn_set_schedule and attn_set_key_groups (0 / -1:
+// the library's choice).
 int attn_sched_rows_per_wave();   // 0, 32 or 64
 int attn_sched_head_group();      // -1, 0 (one group) or n >= 1
+int attn_sched_key_groups();      // -1, 1, 2 or 4
 
 int attn_launch_bf16(const AttnLaunch& a);
-int attn_launch_bf16_d64(const AttnLaunch& a, bool rows32);   // dense d = 64 (attn_fwd_bf16_d64.hip)
+int attn_launch_bf16_d64(const AttnLaunch& a, bool rows32, int key_groups);   // dense d = 64 (attn_fwd_bf16_d64.hip)
 int attn_launch_bwd_bf16(const AttnBwdLaunch& a);
 int attn_launch_f32(const AttnLaunch& a);
 

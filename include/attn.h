@@ -84,7 +84,13 @@ enum attn_status {
  * Tile shape: bf16 calls pick 64 or 32 query rows per wave from the shape (32 for a
  * grid too small to fill the device twice or a window narrower than 4096 keys), and
  * run workgroups in groups of heads whose K and V fit in half the device's 256 MB
- * Infinity Cache.  attn_set_schedule forces either choice; no choice changes a result.
+ * Infinity Cache.  attn_set_schedule forces either choice; neither changes a result
+ * beyond the rounding of the bf16 probabilities.  When the query blocks alone
+ * would leave the device short of work (no mask or causal, at most one or two
+ * workgroups per compute unit), the waves of a workgroup also split its keys into
+ * 2 or 4 key groups whose softmax states are merged exactly at the end (the merge
+ * of local attention results of the Mosaic long-sequence page, §2.1, applied inside
+ * the workgroup); attn_set_key_groups forces that choice.
  *
  * Errors: returns ATTN_OK (0) or a negative attn_status.  Argument errors are
  * detected on the host before anything is enqueued, so nothing is written on such
@@ -290,6 +296,28 @@ int attn_fwd_block_sparse_check_args(const void* q, const void* k, const void* v
  * schedule they were launched with.
  */
 int attn_set_schedule(int rows_per_wave, int head_group);
+
+/*
+ * attn_set_key_groups - force the number of key groups of the bf16 forward with no
+ * mask or the causal mask, process-wide, for every later attn_fwd call (a tuning
+ * and test switch like attn_set_schedule).  With g key groups the four waves of a
+ * workgroup form 4 / g sets of query rows times g sets of key tiles (tile t_lo +
+ * g u + j for group j at step u); each group keeps its own running maximum and sums,
+ * and the groups are merged at the end with weights 2^(m_j - max m).  The result is
+ * the same attention up to the rounding of the bf16 probabilities, which are
+ * taken against each group's own maximum.
+ *
+ *   key_groups  1 (never split the keys), 2 or 4, or -1 for the library's own
+ *               choice (the default).  Rows per wave come from attn_set_schedule
+ *               when it forces them, else 32 for 2 groups at d = 64 and 64
+ *               otherwise.  The band masks always use one group.  With -1 and a
+ *               forced rows_per_wave, keys are split only where the library's own
+ *               choice has those rows per wave.
+ *
+ * Returns ATTN_OK, or ATTN_ERR_BAD_SHAPE for another value (then nothing changes).
+ * Safe to call from any thread; calls already enqueued keep their setting.
+ */
+int attn_set_key_groups(int key_groups);
 
 /* attn_strerror - static, NUL-terminated text for a status code (never NULL). */
 const char* attn_strerror(int status);

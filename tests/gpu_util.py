@@ -104,15 +104,18 @@ def run_case(B, H, N, d, dtype, mask, window=0, scale=None, seed=0, q_mult=1.0, 
     say(f"[gpu] {label}")
     q, k, v = make_qkv(B, H, N, d, tdt, seed=seed, q_mult=q_mult, device=gen_device)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
-    # bf16: each tile shape the library can pick (32 or 64 query rows per wave),
-    # forced in turn, against the one oracle result
-    variants = ROWS_PER_WAVE if (dtype == "bf16" and rows_per_wave is None) else (rows_per_wave,)
+    # bf16: each tile shape the library can pick (32 or 64 query rows per wave, with
+    # the library's key groups or one key group), forced in turn, against the one
+    # oracle result
+    rows = ROWS_PER_WAVE if (dtype == "bf16" and rows_per_wave is None) else (rows_per_wave,)
+    groups = ("auto", "1") if (dtype == "bf16" and mask in ("none", "causal")) else (None,)
     outs = []
-    for rpw in variants:
-        with forced_rows_per_wave(rpw):
-            out, lse = attn.fwd(qd, kd, vd, mask=mask, window=window, scale=scale)
-            torch.cuda.synchronize()
-        outs.append((rpw, out, lse))
+    for rpw in rows:
+        for kg in groups:
+            with forced_rows_per_wave(rpw), forced_key_groups(kg):
+                out, lse = attn.fwd(qd, kd, vd, mask=mask, window=window, scale=scale)
+                torch.cuda.synchronize()
+            outs.append((f"{rpw or 'auto'} key groups={kg or 'auto'}", out, lse))
     qn, kn, vn = to_np(q), to_np(k), to_np(v)
     if n_rows is None or n_rows >= N:
         rows = None
@@ -121,15 +124,15 @@ def run_case(B, H, N, d, dtype, mask, window=0, scale=None, seed=0, q_mult=1.0, 
                                    for h in range(H)]) for b in range(B)])
     O_ref, L_ref, rows = oracle(qn, kn, vn, scale, mk, window, rows)
     res = None
-    for rpw, out, lse in outs:
-        res = compare(out, lse, O_ref, L_ref, rows, dtype, f"{label} rows/wave={rpw or 'auto'}")
+    for shape, out, lse in outs:
+        res = compare(out, lse, O_ref, L_ref, rows, dtype, f"{label} rows/wave={shape}")
     return res
 
 
 ROWS_PER_WAVE = ("32", "64")
 
 
-_SCHED = {"rows_per_wave": 0, "head_group": -1}   # what attn_set_schedule was last given
+_SCHED = {"rows_per_wave": 0, "head_group": -1, "key_groups": -1}   # what the library was last given
 
 
 class _forced:
@@ -143,15 +146,20 @@ class _forced:
     def __enter__(self):
         self.old = _SCHED[self.key]
         if self.value is not None:
-            # "auto": the library's own choice (rows per wave 0, head group -1)
+            # "auto": the library's own choice (rows per wave 0, head group and key groups -1)
             _SCHED[self.key] = (0 if self.key == "rows_per_wave" else -1) if self.value == "auto" else int(self.value)
-            assert attn.attn_set_schedule(_SCHED["rows_per_wave"], _SCHED["head_group"]) == 0
+            _apply()
         return self
 
     def __exit__(self, *exc):
         _SCHED[self.key] = self.old
-        assert attn.attn_set_schedule(_SCHED["rows_per_wave"], _SCHED["head_group"]) == 0
+        _apply()
         return False
+
+
+def _apply():
+    assert attn.attn_set_schedule(_SCHED["rows_per_wave"], _SCHED["head_group"]) == 0
+    assert attn.attn_set_key_groups(_SCHED["key_groups"]) == 0
 
 
 def forced_rows_per_wave(rpw):
@@ -162,3 +170,8 @@ def forced_rows_per_wave(rpw):
 def forced_head_group(g):
     """Force the head-group size (n heads, 0 for one group; None: the library's choice)."""
     return _forced("head_group", g)
+
+
+def forced_key_groups(g):
+    """Force 1, 2 or 4 key groups of the bf16 forward (None: the library's choice)."""
+    return _forced("key_groups", g)
