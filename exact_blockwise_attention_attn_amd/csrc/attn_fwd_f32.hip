@@ -7,17 +7,19 @@
 // exact to fp32 even for large scores; probabilities and the V accumulation are
 // fp32.
 //
-// A workgroup owns 64 query rows; each row is owned by D/64 neighbouring lanes
-// holding 64 of its dimensions, whose partial dot products are combined with a
-// lane shuffle.  The 256 threads form KS = 256 / (64 D/64) groups of such lanes,
-// and group g takes every KS-th key tile of the workgroup's range, so the serial
-// chain of a row is 1/KS of its keys.  K/V tiles of 32 keys are staged in LDS, one
-// pair per group (lanes of one half read the same key row: an LDS broadcast), and
-// each group keeps a running maximum and sum per row.  At the end the groups'
-// partial results are combined exactly (each rescaled to the common maximum) and
-// normalised once ("Blockwise Parallel Transformer in PyTorch", the
+// A workgroup is eight waves, one per key group; all of them hold the same 8 query
+// rows, each row spread over 8 neighbouring lanes with d / 8 of its dimensions,
+// whose partial dot products meet in a lane butterfly (every lane of the row ends
+// with the same bits).  Key group g takes every eighth key tile of the workgroup's
+// range (tiles of TK keys, staged by the group's own wave in LDS with K widened to
+// fp64 once, so the lanes read fp64 operands; no barrier between rounds), keeping
+// its own running maximum and sum per row.  At the end
+// the groups' partial results are combined exactly (each rescaled to the common
+// maximum) and normalised once ("Blockwise Parallel Transformer in PyTorch", the
 // blockwise_attention example and its numerical-stability pitfall; Mosaic
-// long-sequence attention page, §3.2 and §5.1).
+// long-sequence attention page, §3.2 and §5.1).  8 lanes per row and 8 rows per
+// workgroup keep the serial chain of a lane short and the grid wide: the small
+// shapes this path serves are latency-bound.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,9 +28,7 @@
 
 namespace attn_f32 {
 
-constexpr int ROWS = 64;   // query rows per workgroup
-constexpr int TK = 32;     // keys per LDS tile
-constexpr int DD = 64;     // dimensions per lane
+constexpr int KS = 8;      // key groups, one wave each
 
 template <int MASK>
 __device__ __forceinline__ bool key_allowed(int qi, int kj, int N, int window) {
@@ -39,28 +39,40 @@ __device__ __forceinline__ bool key_allowed(int qi, int kj, int N, int window) {
     return true;
 }
 
-constexpr int NTHREADS = 256;
+constexpr int NTHREADS = 64 * KS;
+
+template <int D>
+struct F32Cfg {
+    static constexpr int DL = D / 8;                 // dimensions per lane
+    static constexpr int SPLIT = D / DL;             // lanes per row
+    static constexpr int ROWS = 64 / SPLIT;          // query rows per workgroup
+    static constexpr int TK = D == 64 ? 8 : 4;       // keys per LDS tile
+    static constexpr int KPITCH = DL + 2;            // fp64 words per (key, lane part) in LDS (padded: no bank conflicts)
+    static constexpr int VPITCH = DL + 4;            // fp32 words per (key, lane part)
+    static constexpr int KWORDS = TK * SPLIT * KPITCH;
+    static constexpr int VWORDS = TK * SPLIT * VPITCH;
+};
 
 template <int D, int MASK>
 __global__ __launch_bounds__(NTHREADS)
 void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
                 float* __restrict__ O, float* __restrict__ LSE, int BH, int N, int nqt,
                 float c_log2, int negate_q, int window) {
-    constexpr int SPLIT = D / DD;             // lanes per row
-    constexpr int GT = ROWS * SPLIT;          // threads of one key group
-    constexpr int KS = NTHREADS / GT;         // key groups
-    constexpr int TILE = TK * D;              // floats of one K or V tile
-    // per group a K and a V tile; reused at the end for the groups' partial results
-    __shared__ __attribute__((aligned(16))) float smem[2 * KS * TILE];
-    static_assert((KS - 1) * GT * (DD + 4) <= 2 * KS * TILE, "merge area fits the tile buffers");
+    using C = F32Cfg<D>;
+    constexpr int DL = C::DL, SPLIT = C::SPLIT, ROWS = C::ROWS, TK = C::TK;
+    // per group a K tile (fp64) and a V tile (fp32); the K area is reused at the end
+    // for the groups' partial results
+    __shared__ __attribute__((aligned(16))) double ksm[KS * C::KWORDS];
+    __shared__ __attribute__((aligned(16))) float vsm[KS * C::VWORDS];
+    static_assert((KS - 1) * 64 * (DL + 4) * 4 <= KS * C::KWORDS * 8, "merge area fits the K tiles");
 
     const int tid = threadIdx.x;
-    const int grp = tid / GT;                 // which key group
-    const int lt = tid - grp * GT;
-    const int part = lt % SPLIT;              // which 64 dimensions
-    const int row = lt / SPLIT;
-    float* Ks = smem + grp * 2 * TILE;
-    float* Vs = Ks + TILE;
+    const int grp = tid >> 6;                 // key group (wave)
+    const int lane = tid & 63;
+    const int part = lane % SPLIT;            // which DL dimensions
+    const int row = lane / SPLIT;
+    double* Ks = ksm + grp * C::KWORDS;
+    float* Vs = vsm + grp * C::VWORDS;
     const int id = blockIdx.x;
     const int rank = id / BH;
     const int bh = id - rank * BH;
@@ -69,14 +81,16 @@ void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const 
     const int my_q = q0 + row;
     const int qrow = min(my_q, N - 1);
     const size_t head = (size_t)bh * N * D;
-    const int dof = part * DD;
+    const int dof = part * DL;
 
-    float q[DD], acc[DD];
+    double q[DL];
+    float acc[DL];
     const float sgn = negate_q ? -1.f : 1.f;
 #pragma unroll
-    for (int c = 0; c < DD; c += 4) {
+    for (int c = 0; c < DL; c += 4) {
         const float4 x = *reinterpret_cast<const float4*>(Q + head + (size_t)qrow * D + dof + c);
-        q[c] = sgn * x.x; q[c + 1] = sgn * x.y; q[c + 2] = sgn * x.z; q[c + 3] = sgn * x.w;
+        q[c] = (double)(sgn * x.x); q[c + 1] = (double)(sgn * x.y);
+        q[c + 2] = (double)(sgn * x.z); q[c + 3] = (double)(sgn * x.w);
         acc[c] = acc[c + 1] = acc[c + 2] = acc[c + 3] = 0.f;
     }
     double m = -INFINITY;      // running max of c_log2 * s (log2 domain)
@@ -90,102 +104,116 @@ void fwd_kernel(const float* __restrict__ Q, const float* __restrict__ K, const 
     if (MASK == ATTN_MASK_CAUSAL_WINDOW) { lo = max(0, q0 - window) / TK; hi = min(last, r1 / TK); }
     const double c = (double)c_log2;
 
-    // rounds: group g takes tile t0 + g; every group passes the same barriers
-    for (int t0 = lo; t0 <= hi; t0 += KS) {
-        const int t = t0 + grp;
-        const bool mine = t <= hi;
+    // Group g takes tiles lo + g, lo + g + KS, ...  A group stages and reads only its
+    // own tiles, so its rounds need no barrier (LDS operations of one wave complete
+    // in order); the next tile is fetched into registers before the current one is
+    // used, so its load latency hides behind the arithmetic.
+    constexpr int NLD = TK * D / (64 * 4);    // float4 loads per lane per tile and tensor
+    float4 kreg[NLD], vreg[NLD];
+    auto fetch = [&](int t) __attribute__((always_inline)) {
         const int key0 = t * TK;
-        if (mine) {
-            for (int e = lt * 4; e < TILE; e += GT * 4) {
-                const int kr = e / D, col = e % D;
-                float4 kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-                if (key0 + kr < N) {
-                    kv = *reinterpret_cast<const float4*>(K + head + (size_t)(key0 + kr) * D + col);
-                    vv = *reinterpret_cast<const float4*>(V + head + (size_t)(key0 + kr) * D + col);
-                }
-                *reinterpret_cast<float4*>(Ks + e) = kv;
-                *reinterpret_cast<float4*>(Vs + e) = vv;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+            const int e = (i * 64 + lane) * 4;
+            const int kr = e / D, col = e % D;
+            kreg[i] = vreg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (key0 + kr < N) {
+                kreg[i] = *reinterpret_cast<const float4*>(K + head + (size_t)(key0 + kr) * D + col);
+                vreg[i] = *reinterpret_cast<const float4*>(V + head + (size_t)(key0 + kr) * D + col);
             }
         }
-        __syncthreads();
-        if (mine) {
-            double s[TK];
-            double mt = -INFINITY;
+    };
+    if (lo + grp <= hi) fetch(lo + grp);
+    for (int t = lo + grp; t <= hi; t += KS) {
+        // stage: element e = (key kr, column col) -> (kr, part col / DL, col % DL)
 #pragma unroll
-            for (int j = 0; j < TK; ++j) {
-                double dot = 0.0;
-#pragma unroll
-                for (int cc = 0; cc < DD; ++cc) dot = __builtin_fma((double)q[cc], (double)Ks[j * D + dof + cc], dot);
-                if (SPLIT == 2) dot += __shfl_xor(dot, 1);
-                s[j] = key_allowed<MASK>(my_q, key0 + j, N, window) ? dot * c : -INFINITY;
-                mt = fmax(mt, s[j]);
-            }
-            const double m_new = fmax(m, mt);
-            const double base = (m_new == -INFINITY) ? 0.0 : m_new;
-            const float alpha = __builtin_amdgcn_exp2f((float)(m - base));
-            l *= alpha;
-#pragma unroll
-            for (int cc = 0; cc < DD; ++cc) acc[cc] *= alpha;
-#pragma unroll
-            for (int j = 0; j < TK; ++j) {
-                const float p = __builtin_amdgcn_exp2f((float)(s[j] - base));
-                l += p;
-#pragma unroll
-                for (int cc = 0; cc < DD; ++cc) acc[cc] = __builtin_fmaf(p, Vs[j * D + dof + cc], acc[cc]);
-            }
-            m = m_new;
+        for (int i = 0; i < NLD; ++i) {
+            const int e = (i * 64 + lane) * 4;
+            const int kr = e / D, col = e % D;
+            const int slot = kr * SPLIT + col / DL, cc = col % DL;
+            double* kd = Ks + slot * C::KPITCH + cc;
+            kd[0] = (double)kreg[i].x; kd[1] = (double)kreg[i].y; kd[2] = (double)kreg[i].z; kd[3] = (double)kreg[i].w;
+            *reinterpret_cast<float4*>(Vs + slot * C::VPITCH + cc) = vreg[i];
         }
-        __syncthreads();
+        if (t + KS <= hi) fetch(t + KS);
+        const int key0 = t * TK;
+        double s[TK];
+        double mt = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < TK; ++j) {
+            const double* kr = Ks + (j * SPLIT + part) * C::KPITCH;
+            double dot = 0.0;
+#pragma unroll
+            for (int cc = 0; cc < DL; ++cc) dot = __builtin_fma(q[cc], kr[cc], dot);
+#pragma unroll
+            for (int o = 1; o < SPLIT; o <<= 1) dot += __shfl_xor(dot, o);
+            s[j] = key_allowed<MASK>(my_q, key0 + j, N, window) ? dot * c : -INFINITY;
+            mt = fmax(mt, s[j]);
+        }
+        const double m_new = fmax(m, mt);
+        const double base = (m_new == -INFINITY) ? 0.0 : m_new;
+        const float alpha = __builtin_amdgcn_exp2f((float)(m - base));
+        l *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < DL; ++cc) acc[cc] *= alpha;
+#pragma unroll
+        for (int j = 0; j < TK; ++j) {
+            const float p = __builtin_amdgcn_exp2f((float)(s[j] - base));
+            l += p;
+            const float* vr = Vs + (j * SPLIT + part) * C::VPITCH;
+#pragma unroll
+            for (int cc = 0; cc < DL; ++cc) acc[cc] = __builtin_fmaf(p, vr[cc], acc[cc]);
+        }
+        m = m_new;
     }
+    __syncthreads();     // every group is done with its tiles before the merge reuses the K area
 
     // combine the groups: groups 1.. park (acc, l, m) in LDS, group 0 rescales and sums
-    if (KS > 1) {
-        float* slot = smem + ((grp - 1) * GT + lt) * (DD + 4);
-        if (grp > 0) {
+    float* const park = reinterpret_cast<float*>(ksm);
+    if (grp > 0) {
+        float* const slot = park + ((grp - 1) * 64 + lane) * (DL + 4);
 #pragma unroll
-            for (int cc = 0; cc < DD; cc += 4)
-                *reinterpret_cast<float4*>(slot + cc) = make_float4(acc[cc], acc[cc + 1], acc[cc + 2], acc[cc + 3]);
-            slot[DD] = l;
-            *reinterpret_cast<double*>(slot + DD + 2) = m;
-        }
-        __syncthreads();
-        if (grp == 0) {
-            double M = m;
-#pragma unroll
-            for (int g = 1; g < KS; ++g) M = fmax(M, *reinterpret_cast<const double*>(smem + ((g - 1) * GT + lt) * (DD + 4) + DD + 2));
-            const float w0 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((float)(m - M));
-            l *= w0;
-#pragma unroll
-            for (int cc = 0; cc < DD; ++cc) acc[cc] *= w0;
-#pragma unroll
-            for (int g = 1; g < KS; ++g) {
-                const float* sg = smem + ((g - 1) * GT + lt) * (DD + 4);
-                const double mg = *reinterpret_cast<const double*>(sg + DD + 2);
-                const float wg = (mg == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((float)(mg - M));
-                l = __builtin_fmaf(wg, sg[DD], l);
-#pragma unroll
-                for (int cc = 0; cc < DD; ++cc) acc[cc] = __builtin_fmaf(wg, sg[cc], acc[cc]);
-            }
-            m = M;
-        }
+        for (int cc = 0; cc < DL; cc += 4)
+            *reinterpret_cast<float4*>(slot + cc) = make_float4(acc[cc], acc[cc + 1], acc[cc + 2], acc[cc + 3]);
+        slot[DL] = l;
+        *reinterpret_cast<double*>(slot + DL + 2) = m;
     }
-
-    if (grp == 0 && my_q < N) {
-        const float inv = 1.0f / l;
+    __syncthreads();
+    if (grp == 0) {
+        double M = m;
 #pragma unroll
-        for (int cc = 0; cc < DD; cc += 4) {
-            float4 y = {acc[cc] * inv, acc[cc + 1] * inv, acc[cc + 2] * inv, acc[cc + 3] * inv};
-            *reinterpret_cast<float4*>(O + head + (size_t)my_q * D + dof + cc) = y;
+        for (int g = 1; g < KS; ++g) M = fmax(M, *reinterpret_cast<const double*>(park + ((g - 1) * 64 + lane) * (DL + 4) + DL + 2));
+        const float w0 = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((float)(m - M));
+        l *= w0;
+#pragma unroll
+        for (int cc = 0; cc < DL; ++cc) acc[cc] *= w0;
+#pragma unroll
+        for (int g = 1; g < KS; ++g) {
+            const float* sg = park + ((g - 1) * 64 + lane) * (DL + 4);
+            const double mg = *reinterpret_cast<const double*>(sg + DL + 2);
+            const float wg = (mg == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((float)(mg - M));
+            l = __builtin_fmaf(wg, sg[DL], l);
+#pragma unroll
+            for (int cc = 0; cc < DL; ++cc) acc[cc] = __builtin_fmaf(wg, sg[cc], acc[cc]);
         }
-        if (part == 0)
-            LSE[(size_t)bh * N + my_q] =
-                (float)((m + (double)__builtin_amdgcn_logf(l)) * 0.69314718055994530942);
+        m = M;
+        if (my_q < N) {
+            const float inv = 1.0f / l;
+#pragma unroll
+            for (int cc = 0; cc < DL; cc += 4) {
+                float4 y = {acc[cc] * inv, acc[cc + 1] * inv, acc[cc + 2] * inv, acc[cc + 3] * inv};
+                *reinterpret_cast<float4*>(O + head + (size_t)my_q * D + dof + cc) = y;
+            }
+            if (part == 0)
+                LSE[(size_t)bh * N + my_q] =
+                    (float)((m + (double)__builtin_amdgcn_logf(l)) * 0.69314718055994530942);
+        }
     }
 }
 
 template <int D, int MASK>
 static int launch(const AttnLaunch& a) {
-    const int nqt = (a.N + ROWS - 1) / ROWS;
+    const int nqt = (a.N + F32Cfg<D>::ROWS - 1) / F32Cfg<D>::ROWS;
     const long long grid = (long long)nqt * a.B * a.H;
     hipLaunchKernelGGL((fwd_kernel<D, MASK>), dim3((unsigned)grid), dim3(NTHREADS), 0,
                        (hipStream_t)a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
