@@ -259,9 +259,7 @@ def main_decode(args, torch, attn):
         attn.fwd_kv(q, k, v, q_offset=off, mask=wl.mask, window=wl.window, scale=wl.softmax_scale, out=out,
                     lse=lse, workspace=ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args, torch)
     stream = torch.cuda.current_stream()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
@@ -364,9 +362,7 @@ def main_sparse(args, torch, attn):
     def step():
         attn.fwd_block_sparse(q, k, v, lay_d, causal=wl.causal, scale=wl.softmax_scale, out=out, lse=lse)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args, torch)
     stream = torch.cuda.current_stream()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
@@ -409,11 +405,38 @@ def main_sparse(args, torch, attn):
     print(json.dumps(rec), flush=True)
 
 
+WARMUP_MIN_STEPS = 5
+WARMUP_MIN_S = 0.2
+
+
+def warm_up(step, args, torch):
+    """Untimed warm-up: exactly --warmup steps when given; by default at least
+    WARMUP_MIN_STEPS steps and at least WARMUP_MIN_S seconds of them, so that short
+    steps (tens of microseconds) are timed at the clock a sustained run reaches.
+    Records the count in args.warmup."""
+    if args.warmup is not None:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        return
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(WARMUP_MIN_STEPS):
+            step()
+        n += WARMUP_MIN_STEPS
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= WARMUP_MIN_S:
+            break
+    args.warmup = n
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help=f"untimed warm-up steps (default: at least {WARMUP_MIN_STEPS} and {WARMUP_MIN_S} s of them)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--pass", dest="which", choices=["fwd", "bwd", "decode", "sparse"], default="fwd")
     ap.add_argument("--seed", type=int, default=0)
@@ -458,11 +481,12 @@ def main():
         n = args.copy_calibration * (1 << 20) // 4
         src = torch.randn(n, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(args.warmup + args.steps):
+        launches = (args.warmup if args.warmup is not None else WARMUP_MIN_STEPS) + args.steps
+        for _ in range(launches):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
-                          "launches": args.warmup + args.steps}), flush=True)
+                          "launches": launches}), flush=True)
         return
 
     q, k, v = make_qkv(wl.B, wl.H, wl.N, wl.d, wl.torch_dtype, seed=args.seed, device="cuda")
@@ -490,9 +514,7 @@ def main():
         def step():
             attn.fwd(q, k, v, mask=wl.mask, window=wl.window, scale=wl.softmax_scale, out=out, lse=lse)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args, torch)
     # the kernel runs on torch's current stream; the events are recorded on that stream,
     # one before every step and one after the last, so each step's duration is known
     stream = torch.cuda.current_stream()

@@ -161,7 +161,9 @@ struct SplitArgs {
 // instantiations and runs one wave per SIMD; two waves per SIMD let one wave's
 // softmax overlap the other's matrix instructions (+23% on causal cases, +35% on the
 // narrow window).  The 64-row shapes need the whole register file; at d = 64 the
-// 32-row kernels fit two waves anyway and the cap measured slower.
+// 32-row kernels fit two waves anyway and the cap measured slower.  Key-group
+// kernels: the d = 64 32-row ones keep two waves per SIMD (the cap costs them no
+// spill); at d = 128 they run without the cap (under it the merge spills).
 // Block-sparse layouts (internal mask kinds of the kernel; the C ABI has its own
 // entry point): the allowed keys of a 128-row query block are the 128-key blocks
 // its layout row marks, intersected with j <= i for the causal variant.
@@ -179,7 +181,7 @@ struct BlockArgs {
 
 template <int D, int QB, int MASK, bool SPLIT, int KG>
 constexpr int min_waves_per_simd() {
-    return ((D == 128 && QB == 1) || (D == 64 && QB == 1 && KG > 1)) ? 2 : 1;
+    return ((D == 128 && QB == 1 && KG == 1) || (D == 64 && QB == 1 && KG > 1)) ? 2 : 1;
 }
 
 template <int D, int QB, int KB, int MASK, bool SPLIT = false, int KG = 1>
@@ -376,6 +378,23 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         if constexpr (KG > 1) return min(tile_of(u), t_hi);
         else return tile_of(u);
     };
+    // This wave's own steps wu_lo .. wu_hi: the tiles that hold an allowed key for one
+    // of its rows (the workgroup's range is the union over its waves, so at a band's
+    // ends or past a causal diagonal a wave's range is shorter).  Outside them the
+    // wave only loads its share of the tiles and meets the barriers; the step before
+    // its first computes that step's scores, the step after its last that step's V
+    // product.  Key groups and block layouts keep the whole range.
+    int wu_lo = 0, wu_hi = n_steps - 1;
+    if constexpr (KG == 1 && !BLK) {
+        if (qw0 >= N) {
+            wu_lo = n_steps;                              // every row past the end: no step
+        } else {
+            int wlo, whi;
+            tile_range<MASK, BC>(qw0 + qoff, min(qw0 + C::RW, N) - 1 + qoff, Nk, window, wlo, whi);
+            wu_lo = __builtin_amdgcn_readfirstlane(max(wlo, t_lo) - t_lo);
+            wu_hi = __builtin_amdgcn_readfirstlane(min(whi, t_hi) - t_lo);
+        }
+    }
 
     // direct HBM -> LDS load of tile t of one tensor into `dst` (this wave's share):
     // per-lane offsets fixed for the kernel, the tile's offset a scalar
@@ -675,8 +694,10 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
 #pragma unroll
         for (int s = 0; s < NS; ++s) settle_qa(qreg[b][s]);
     __syncthreads();
-    scores(IntC<0>{}, kb0);
-    settle_scores(IntC<0>{});
+    if (wu_lo == 0) {
+        scores(IntC<0>{}, kb0);
+        settle_scores(IntC<0>{});
+    }
     __syncthreads();     // every wave is done with K(t_lo) before tile 0 refills its buffer
 
     auto iter = [&](auto parity, int u) __attribute__((always_inline)) {
@@ -747,14 +768,50 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
     };
+    // a step outside the wave's own range: its loads, the wait and the barrier only
+    auto idle = [&](int u) __attribute__((always_inline)) {
+        if (u + 2 < n_steps) dma(krs, tile_ld(u + 2), (u & 1) ? kb1 : kb0);
+        dma(vrs, tile_ld(u), (u & 1) ? vb1 : vb0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
+    // the step before the wave's first (its scores) or after its last (its V product)
+    auto edge = [&](auto parity, int u, bool first) __attribute__((always_inline)) {
+        constexpr int B = decltype(parity)::value;
+        constexpr int X = 1 - B;
+        if (u + 2 < n_steps) dma(krs, tile_ld(u + 2), B ? kb1 : kb0);
+        dma(vrs, tile_ld(u), B ? vb1 : vb0);
+        if (first) {
+            scores(IntC<X>{}, B ? kb0 : kb1);
+            settle_scores(IntC<X>{});
+        } else {
+            pv(IntC<X>{}, B ? vb0 : vb1);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+    };
     int u = 0;
-    for (; u + 1 < n_steps; u += 2) {
+    for (; u < wu_lo - 1; ++u) idle(u);
+    if (u == wu_lo - 1) {
+        if (u & 1) edge(IntC<1>{}, u, true); else edge(IntC<0>{}, u, true);
+        ++u;
+    }
+    if (u <= wu_hi && (u & 1)) iter(IntC<1>{}, u++);
+    for (; u + 1 <= wu_hi; u += 2) {
         iter(IntC<0>{}, u);
         iter(IntC<1>{}, u + 1);
     }
-    if (u < n_steps) iter(IntC<0>{}, u++);
-    // closing step: the V product of the last step (its V in vbuf[(n_steps - 1) % 2])
-    if (u & 1) pv(IntC<0>{}, vb0); else pv(IntC<1>{}, vb1);
+    if (u <= wu_hi) iter(IntC<0>{}, u++);
+    if (u == wu_hi + 1 && u < n_steps) {
+        if (u & 1) edge(IntC<1>{}, u, false); else edge(IntC<0>{}, u, false);
+        ++u;
+    }
+    for (; u < n_steps; ++u) idle(u);
+    // closing step: the V product of the last step (its V in vbuf[(n_steps - 1) % 2]),
+    // for a wave whose own steps reach it
+    if (wu_hi == n_steps - 1) {
+        if (u & 1) pv(IntC<0>{}, vb0); else pv(IntC<1>{}, vb1);
+    }
 
     // ---- key groups: merge the softmax states of groups 1 .. KG-1 into group 0.  With
     // M = max over groups of the running maximum m_g and weight a_g = 2^(m_g - M) (0

@@ -7,7 +7,9 @@ written by an LDS load (waited for by s_waitcnt), (b) the Q operands written int
 AGPRs once, long before, and (c) its own chain accumulator.  A vector-ALU write to
 one of its source registers in the few instructions before it would need wait
 states nobody inserted.  This module finds such writes; registers overwritten by
-an MFMA in between do not count (the value then comes from that MFMA).
+an MFMA or a memory load into registers in between do not count (the value then
+comes from that instruction, whose completion s_waitcnt or the MFMA interlock
+orders).
 """
 from __future__ import annotations
 
@@ -45,6 +47,15 @@ def _instructions(asm_text: str):
         yield op, [o.strip() for o in s[len(op):].split(",") if o.strip()], inasm, s
 
 
+def _loads_into_registers(op: str, ops: list[str]) -> bool:
+    """A memory load whose first operand is its destination: LDS, global, scratch
+    or buffer loads, except the direct-to-LDS buffer form (its first operand is an
+    address)."""
+    if op.startswith(("ds_read", "global_load", "scratch_load", "flat_load")):
+        return True
+    return op.startswith("buffer_load") and not any(o.split()[-1] == "lds" or o.endswith(" lds") for o in ops)
+
+
 def check(asm_text: str) -> tuple[int, list[str]]:
     """Return (asm MFMAs checked, list of suspicious findings).
 
@@ -67,6 +78,9 @@ def check(asm_text: str) -> tuple[int, list[str]]:
             dst = _regs(pops[0])
             if pop.startswith("v_mfma"):
                 live -= dst              # value now comes from that MFMA
+                continue
+            if _loads_into_registers(pop, pops):
+                live -= dst              # value now comes from that load
                 continue
             if pop.startswith("v_") and dst & live:
                 found.append(f"before: {ptext} -> {text}")

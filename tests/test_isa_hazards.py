@@ -28,6 +28,25 @@ def test_checker_finds_planted_hazard():
     assert n == 1 and len(found) == 1
 
 
+def test_checker_ignores_a_write_overwritten_by_a_load():
+    # the source register was last written by an LDS load (waited for), not by the
+    # earlier vector-ALU instruction; a direct-to-LDS buffer load only reads its
+    # address register and does not count as a rewrite
+    text = "\n".join([
+        "v_lshl_add_u32 v18, v18, 8, v112",
+        "buffer_load_dwordx4 v18, s[4:7], s24 offen lds",
+        "ds_read_b128 v[18:21], v121",
+        "s_waitcnt lgkmcnt(0)",
+        ";;#ASMSTART",
+        "v_mfma_f32_32x32x16_bf16 v[34:49], v[18:21], a[92:95], 0",
+        ";;#ASMEND",
+    ])
+    assert isa_hazards.check(text) == (1, [])
+    planted = text.replace("ds_read_b128 v[18:21], v121", "buffer_load_dwordx4 v19, s[4:7], s24 offen lds")
+    n, found = isa_hazards.check(planted)
+    assert n == 1 and len(found) == 1 and found[0].startswith("before")
+
+
 def test_checker_finds_result_register_reused_too_early():
     # an asm MFMA whose result the compiler thinks dead: its registers handed to a
     # vector-ALU value while the MFMA still writes them
