@@ -153,7 +153,7 @@ def cpu_baseline(wl, q, k, v, budget_s=20.0):
     except Exception:  # noqa: BLE001
         threads = 1
         blas = "?"
-    rows = sample_rows(wl.N, min(wl.N, 1024), seed=12345, window=wl.window)
+    rows = sample_rows(wl.N, min(wl.N, 4096), seed=12345, window=wl.window)
     mk = wl.mask_kind
     flops = 0
     heads = 0

@@ -225,13 +225,19 @@ def fwd(q, k, v, mask="none", window=0, scale=None, out=None, lse=None, stream=N
     mk = MASKS[mask] if isinstance(mask, str) else int(mask)
     dt = ATTN_DTYPE_BF16 if q.dtype == torch.bfloat16 else ATTN_DTYPE_F32
     s, raw = _stream(stream, q.device)
-    with torch.cuda.device(q.device), torch.cuda.stream(s):
-        if out is None:
-            out = torch.empty_like(q)
-        if lse is None:
-            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out is not None and lse is not None and torch.cuda.current_device() == q.device.index:
+        # nothing to allocate and the device is current: launch directly (the
+        # launch-bound small shapes pay for every context switch)
         st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                       B, H, N, d, float(scale), mk, int(window), dt, raw)
+    else:
+        with torch.cuda.device(q.device), torch.cuda.stream(s):
+            if out is None:
+                out = torch.empty_like(q)
+            if lse is None:
+                lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+            st = attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, N, d, float(scale), mk, int(window), dt, raw)
     if st != ATTN_OK:
         raise AttnError(st, attn_strerror(st))
     return out, lse
