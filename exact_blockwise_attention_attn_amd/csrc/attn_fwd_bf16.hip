@@ -569,7 +569,15 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     constexpr int NPM = NKS * GPV;               // V-product (and row-sum) instructions per tile
     constexpr int NSLOT = NSM + NPM;
     constexpr int NEL = 16 * QB;                 // scores per lane per tile (KB = 1)
-    constexpr int NTASK = QB + 1 + NEL + 1;      // lane maxima, vote, scores, sum update
+    // The reference is checked after the probabilities (a vote on their sums) at 32 rows
+    // per wave, before them (a vote on the lane maxima) at 64: there the sums' vote
+    // keeps the scores of S(t) live to the end of the tile, which the full register
+    // file cannot afford (causal B2 H32 N8192 -7%); at 32 rows per wave it saves the
+    // maxima (causal d = 64 H16 N8192 +7%, window +3%).  The block-layout kernels keep
+    // the maxima vote (under their two-waves-per-SIMD cap the sums' vote spills).
+    constexpr bool SUMVOTE = (QB == 1) && !BLK;
+    constexpr int P0 = SUMVOTE ? 0 : QB + 1;     // first probability task
+    constexpr int NTASK = P0 + NEL + 2 + 1;      // [maxima, vote,] scores (three stages), [vote,] sums
     constexpr int KPRE = 3;                      // K operands read before the first slot
     constexpr int VLEAD = 4;                     // slots between a V read and its first use
     static_assert(KB == 1, "the schedule assumes 32-key tiles");
@@ -585,31 +593,57 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     };
 
     // reference state per query block: m_run (log2 domain, -inf before any allowed
-    // key), the exponent offset base_run (m_run, or 0 while m_run = -inf) and
-    // thr_raw = (m_run + TAU) / c, the raw score above which the reference is raised
+    // key) and the exponent offset base_run (m_run, or 0 while m_run = -inf).  ready:
+    // every row of the wave has a reference (wave-uniform; once true, it stays true).
+    // thr_raw (maxima vote) = (m_run + TAU) / c, the raw score above which the reference is raised.
     float base_run[QB], thr_raw[QB];
 #pragma unroll
     for (int b = 0; b < QB; ++b) { base_run[b] = 0.f; thr_raw[b] = -INFINITY; }
     const float inv_c = 1.0f / c_log2;
+    bool ready = false;
+    const float PMAX = __builtin_amdgcn_exp2f(TAU);     // the largest probability against the reference
 
-    // softmax task k of S(t) in sc[X]
-    auto task = [&](auto xc, auto kc, float* mx, float* alpha, float* se, float* sr,
-                    float (*ev)[16], bool& raise_any) __attribute__((always_inline)) {
+    // softmax task k of S(t) in sc[X].
+    // Maxima vote: the lane maxima of the tile, then a wave vote on whether any row's
+    // scores pass its threshold; if so (rare), every row takes its exact running
+    // maximum as reference before the probabilities are taken.
+    // Sums vote: the probabilities are taken against the current reference without
+    // looking at the tile's maximum first; the last task votes on their sums.  A lane
+    // whose probabilities sum to at most 2^TAU holds none above it, so the reference
+    // stands (the common case); otherwise, or when a row meets its first allowed key,
+    // every row takes its exact running maximum and the tile's probabilities are
+    // computed again (rare).
+    auto task = [&](auto xc, auto kc, float* mx, float* alpha, float* se, float* sr, float (*ev)[16],
+                    bool& raise_any, int key0) __attribute__((always_inline)) {
         constexpr int X = decltype(xc)::value;
         constexpr int k = decltype(kc)::value;
-        if constexpr (k < QB) {                              // lane maximum of block k (v_max3 chain)
+        // pack the bf16 pair (r - 1, r) of block b into P^T: keys 8 (r/4) + 4 hl + r % 4,
+        // slab r / 8, position r % 8; the rounded pair's sum when it stays on the VALU
+        auto pack = [&](int b, auto rc, float e0, float e1) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            bf16x2 pa;
+            pa[0] = (__bf16)e0;
+            pa[1] = (__bf16)e1;
+            const uint32_t pb = __builtin_bit_cast(uint32_t, pa);
+            if constexpr (!RSM) {
+                const float lo = __uint_as_float(pb << 16), hi = __uint_as_float(pb & 0xffff0000u);
+                sr[b] = (r == 1) ? lo + hi : sr[b] + lo + hi;
+            }
+            pr[X][b][r >> 3][(r & 7) - 1] = pa[0];
+            pr[X][b][r >> 3][r & 7] = pa[1];
+        };
+        if constexpr (k < P0 && k < QB) {                     // lane maximum of block k (v_max3 chain)
             constexpr int b = k;
             float m = fmaxf(fmaxf(sc[X][b][0][0], sc[X][b][0][1]), sc[X][b][0][2]);
 #pragma unroll
             for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, sc[X][b][0][r]), sc[X][b][0][r + 1]);
             mx[b] = fmaxf(m, sc[X][b][0][15]);
-        } else if constexpr (k == QB) {                      // wave vote: does any row pass its threshold?
+        } else if constexpr (k < P0) {                       // maxima vote
             bool over = false;
 #pragma unroll
             for (int b = 0; b < QB; ++b) { over |= mx[b] > thr_raw[b]; alpha[b] = 1.f; }
             raise_any = __any(over);
             if (raise_any) {
-                // rare: every row of the wave takes its exact running maximum as reference
                 asm volatile("" ::: "memory");
 #pragma unroll
                 for (int b = 0; b < QB; ++b) {
@@ -621,28 +655,75 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                     thr_raw[b] = (m_new + TAU) * inv_c;
                 }
             }
-        } else if constexpr (k < QB + 1 + NEL) {             // one probability
-            constexpr int h = k - QB - 1, b = h / 16, r = h % 16;
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[X][b][0][r], c_log2, -base_run[b]));
-            se[b] = (r == 0) ? e : se[b] + e;
-            ev[b][r] = e;
-            if constexpr (r & 1) {
-                bf16x2 pa;
-                pa[0] = (__bf16)ev[b][r - 1];
-                pa[1] = (__bf16)e;
-#ifdef RSUM_DOT2
-                sr[b] = __builtin_amdgcn_fdot2_f32_bf16(pa, (bf16x2){(__bf16)1.0f, (__bf16)1.0f}, r == 1 ? 0.f : sr[b], false);
-#else
-                // sum of the rounded pair: the two bf16 halves read back as fp32
-                const uint32_t pb = __builtin_bit_cast(uint32_t, pa);
-                if constexpr (!RSM) {
-                    const float lo = __uint_as_float(pb << 16), hi = __uint_as_float(pb & 0xffff0000u);
-                    sr[b] = (r == 1) ? lo + hi : sr[b] + lo + hi;
+        } else if constexpr (k < P0 + NEL + 2) {
+            // The probabilities in three stages, each a step behind the previous one:
+            // task P0 + h takes the exponent argument of score h, the exponential of score
+            // h - 1 and the sums and packing of score h - 2.  One task runs per matrix
+            // instruction, so the three operations of a task are independent and each
+            // waits on a result from an earlier slot, not on its own neighbour.
+            constexpr int hc = k - P0 - 2;                   // sums and packing
+            if constexpr (hc >= 0 && hc < NEL) {
+                constexpr int b = hc / 16, r = hc % 16;
+                const float e = ev[b][r];
+                se[b] = (r == 0) ? e : se[b] + e;
+                if constexpr (r & 1) pack(b, IntC<r>{}, ev[b][r - 1], e);
+            }
+            constexpr int hb = k - P0 - 1;                   // exponential
+            if constexpr (hb >= 0 && hb < NEL) {
+                constexpr int b = hb / 16, r = hb % 16;
+                ev[b][r] = __builtin_amdgcn_exp2f(ev[b][r]);
+            }
+            constexpr int ha = k - P0;                       // exponent argument
+            if constexpr (ha < NEL) {
+                constexpr int b = ha / 16, r = ha % 16;
+                ev[b][r] = __builtin_fmaf(sc[X][b][0][r], c_log2, -base_run[b]);
+            }
+        } else if constexpr (SUMVOTE) {                      // sums vote, then the running sums
+            bool over = false;
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                over |= !(se[b] <= PMAX);
+                alpha[b] = 1.f;
+            }
+            if (!ready) {
+                // a row without a reference whose allowed keys meet this tile
+#pragma unroll
+                for (int b = 0; b < QB; ++b)
+                    over |= m_run[b] == -INFINITY &&
+                            (unsigned)(key0 + BC - 1 - key_lo[b]) <= (unsigned)(key_span[b] + BC - 1);
+            }
+            raise_any = __any(over);
+            if (raise_any) {
+                // rare: every row of the wave takes its exact running maximum as reference
+                asm volatile("" ::: "memory");
+                bool have = true;
+#pragma unroll
+                for (int b = 0; b < QB; ++b) {
+                    float m = fmaxf(fmaxf(sc[X][b][0][0], sc[X][b][0][1]), sc[X][b][0][2]);
+#pragma unroll
+                    for (int r = 3; r < 15; r += 2) m = fmaxf(fmaxf(m, sc[X][b][0][r]), sc[X][b][0][r + 1]);
+                    m = fmaxf(m, sc[X][b][0][15]);
+                    const float m_new = fmaxf(m_run[b], swap32_max(m) * c_log2);
+                    const float base = (m_new == -INFINITY) ? 0.f : m_new;
+                    alpha[b] = __builtin_amdgcn_exp2f(m_run[b] - base);   // 0 while m_run = -inf
+                    m_run[b] = m_new;
+                    base_run[b] = base;
+                    have &= m_new != -INFINITY;
+                    // this tile's probabilities again, against the new reference
+                    static_for<0, 16>([&](auto rc) {
+                        constexpr int r = decltype(rc)::value;
+                        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[X][b][0][r], c_log2, -base));
+                        se[b] = (r == 0) ? e : se[b] + e;
+                        ev[b][r] = e;
+                        if constexpr (r & 1) pack(b, rc, ev[b][r - 1], e);
+                    });
                 }
-#endif
-                // keys 8 (r/4) + 4 hl + r % 4: slab r / 8, position r % 8
-                pr[X][b][r >> 3][(r & 7) - 1] = pa[0];
-                pr[X][b][r >> 3][r & 7] = pa[1];
+                ready = !__any(!have);
+            }
+#pragma unroll
+            for (int b = 0; b < QB; ++b) {
+                l_exp[b] = __builtin_fmaf(alpha[b], l_exp[b], se[b]);
+                if constexpr (!RSM) l_rnd[b] = __builtin_fmaf(alpha[b], l_rnd[b], sr[b]);
             }
         } else {                                             // running sums
 #pragma unroll
@@ -718,7 +799,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
         bf16x8 ka[NS], va[NPC];
         __builtin_amdgcn_sched_barrier(0);
         static_for<0, KPRE>([&](auto sc_) { ka[decltype(sc_)::value] = read_k(k_next, decltype(sc_)::value); });
-        task(IntC<B>{}, IntC<0>{}, mx, alpha, se, sr, ev, raise_any);
+        task(IntC<B>{}, IntC<0>{}, mx, alpha, se, sr, ev, raise_any, t * BC);
         __builtin_amdgcn_sched_barrier(0);
         static_for<0, NSLOT>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
@@ -747,7 +828,7 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
             // softmax tasks of slot i: task k (>= 1) runs in slot (k - 1) NSLOT / (NTASK - 1)
             static_for<1, NTASK>([&](auto kc) {
                 constexpr int k = decltype(kc)::value;
-                if constexpr ((k - 1) * NSLOT / (NTASK - 1) == i) task(IntC<B>{}, kc, mx, alpha, se, sr, ev, raise_any);
+                if constexpr ((k - 1) * NSLOT / (NTASK - 1) == i) task(IntC<B>{}, kc, mx, alpha, se, sr, ev, raise_any, t * BC);
             });
             __builtin_amdgcn_sched_barrier(0);
         });
