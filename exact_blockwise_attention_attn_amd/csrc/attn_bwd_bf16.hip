@@ -243,24 +243,40 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[k], dp, 0, 0, 0);
         }
         // per row r of the C layout: query 8 (r/4) + 4 hl + r%4 of the tile; LSE and D
-        // read four rows at a time, right before use
+        // read four rows at a time, right before use.  At d = 64 the element mask runs only
+        // when the tile's queries are not all allowed for every key of the wave.
         bf16x8 pp[2], dsp[2];
         const int rel0 = t * BT + 4 * hl - q_lo;
+        auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const float4 a = *reinterpret_cast<const float4*>(lb + 8 * g + 4 * hl);
-            const float4 b = *reinterpret_cast<const float4*>(db + 8 * g + 4 * hl);
-            const float l2[4] = {a.x, a.y, a.z, a.w}, dd[4] = {b.x, b.y, b.z, b.w};
+            for (int g = 0; g < 4; ++g) {
+                const float4 a = *reinterpret_cast<const float4*>(lb + 8 * g + 4 * hl);
+                const float4 b = *reinterpret_cast<const float4*>(db + 8 * g + 4 * hl);
+                const float l2[4] = {a.x, a.y, a.z, a.w}, dd[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
-            for (int e4 = 0; e4 < 4; ++e4) {
-                const int r = 4 * g + e4;
-                const int qoff = 8 * g + e4;
-                const bool ok = (unsigned)(rel0 + qoff) <= q_span;
-                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2[e4]));
-                const float p = ok ? e : 0.f;
-                const float ds = p * (dp[r] - dd[e4]);
-                pp[r >> 3][r & 7] = (__bf16)p;
-                dsp[r >> 3][r & 7] = (__bf16)ds;
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int r = 4 * g + e4;
+                    const int qoff = 8 * g + e4;
+                    const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l2[e4]));
+                    float p = e;
+                    if constexpr (decltype(masked)::value) p = (unsigned)(rel0 + qoff) <= q_span ? e : 0.f;
+                    const float ds = p * (dp[r] - dd[e4]);
+                    pp[r >> 3][r & 7] = (__bf16)p;
+                    dsp[r >> 3][r & 7] = (__bf16)ds;
+                }
+            }
+        };
+        // (at d = 128 the second copy of this block costs the register-capped kernel
+        // spills: there the mask runs on every tile)
+        if constexpr (D == 128) {
+            probs(IntC<1>{});
+        } else {
+            const int a0 = t * BT - q_lo;              // the whole tile inside this key's queries?
+            if (__any(!(a0 >= 0 && a0 + (BT - 1) <= (int)q_span))) {
+                asm volatile("" ::: "memory");
+                probs(IntC<1>{});
+            } else {
+                probs(IntC<0>{});
             }
         }
         // dV^T += dO_t^T P and dK^T += Q_t^T dS (A operands: transposing reads of the tiles)
@@ -398,15 +414,26 @@ void dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const
             st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qop[k], st, 0, 0, 0);
             dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gop[k], dpt, 0, 0, 0);
         }
+        // the element mask runs only when the tile's keys are not all allowed for every
+        // query of the wave
         bf16x8 dsp[2];
         const int rel0 = t * BT + 4 * hl - k_lo;
+        auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int koff = 8 * (r >> 2) + (r & 3);
-            const bool ok = (unsigned)(rel0 + koff) <= k_span;
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c_log2, -l2));
-            const float p = ok ? e : 0.f;
-            dsp[r >> 3][r & 7] = (__bf16)(p * (dpt[r] - dd));
+            for (int r = 0; r < 16; ++r) {
+                const int koff = 8 * (r >> 2) + (r & 3);
+                const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], c_log2, -l2));
+                float p = e;
+                if constexpr (decltype(masked)::value) p = (unsigned)(rel0 + koff) <= k_span ? e : 0.f;
+                dsp[r >> 3][r & 7] = (__bf16)(p * (dpt[r] - dd));
+            }
+        };
+        const int a0 = t * BT - k_lo;                  // the whole tile inside this query's keys?
+        if (__any(!(a0 >= 0 && a0 + (BT - 1) <= (int)k_span))) {
+            asm volatile("" ::: "memory");
+            probs(IntC<1>{});
+        } else {
+            probs(IntC<0>{});
         }
         // dQ^T += K_t^T dS^T (A operand: transposing reads of the K tile)
 #pragma unroll
