@@ -451,6 +451,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of attention, run a plain device copy of MIB MiB per step (the reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--work-queue", type=int, default=-1, choices=[-1, 0, 1],
+                    help="the bf16 forward's work queue (attn_set_work_queue): 1 on, 0 off, -1 the library's "
+                         "choice")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -468,6 +471,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     attn.load()
+    if attn.attn_set_work_queue(args.work_queue) != 0:
+        raise SystemExit(f"attn_set_work_queue({args.work_queue}) failed")
     if args.which == "decode":
         main_decode(args, torch, attn)
         return
@@ -587,7 +592,7 @@ def main():
                    "pct_of_peak": round(100.0 * tflops / peak, 2), "peak_tflops": peak,
                    "ms_median": round(ms_median, 5), "ms_min": round(ms_min, 5),
                    "tflops_at_median": round(flops / (ms_median * 1e-3) / 1e12, 2),
-                   "cold_l2": bool(args.cold), "wall_s_timed_region": round(wall, 4)},
+                   "cold_l2": bool(args.cold), "work_queue": args.work_queue, "wall_s_timed_region": round(wall, 4)},
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -77,6 +77,8 @@ def load():
     lib.attn_set_schedule.restype = i
     lib.attn_set_key_groups.argtypes = [i]
     lib.attn_set_key_groups.restype = i
+    lib.attn_set_work_queue.argtypes = [i]
+    lib.attn_set_work_queue.restype = i
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_version.argtypes = []
@@ -153,6 +155,12 @@ def attn_set_key_groups(key_groups: int) -> int:
     with no mask or the causal mask (-1 = the library's choice) for later calls;
     returns the status code."""
     return load().attn_set_key_groups(key_groups)
+
+
+def attn_set_work_queue(mode: int) -> int:
+    """C ``attn_set_work_queue``: the bf16 forward's work queue (1 = on, 0 = off,
+    -1 = the library's choice) for later calls; returns the status code."""
+    return load().attn_set_work_queue(mode)
 
 
 def attn_strerror(status: int) -> str:

@@ -7,6 +7,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "attn_launch.h"
 
@@ -247,10 +248,53 @@ static std::atomic<int> g_rows_per_wave{0};
 static std::atomic<int> g_head_group{-1};
 
 static std::atomic<int> g_key_groups{-1};
+static std::atomic<int> g_work_queue{-1};
 
 int attn_sched_rows_per_wave() { return g_rows_per_wave.load(std::memory_order_relaxed); }
 int attn_sched_head_group() { return g_head_group.load(std::memory_order_relaxed); }
 int attn_sched_key_groups() { return g_key_groups.load(std::memory_order_relaxed); }
+int attn_sched_work_queue() { return g_work_queue.load(std::memory_order_relaxed); }
+
+// Work-queue slots of the forward launches (wq_take in attn_tile.h): a device array,
+// one copy per device, whose device address is taken once per device with
+// hipGetSymbolAddress (host code never hands the array's name to a kernel); each
+// launch that uses the queue takes the next of WQ_SLOTS slots in turn.  A slot is
+// left at zero by the last claiming workgroup of the launch that used it, so two
+// launches share a slot only if WQ_SLOTS of them run at once on one device.
+__device__ __align__(256) unsigned attn_wq_pool[WQ_SLOTS * WQ_SLOT_WORDS];
+
+namespace {
+constexpr int WQ_MAX_DEVICES = 64;
+std::mutex g_wq_mu;
+unsigned* g_wq_base[WQ_MAX_DEVICES];
+std::atomic<unsigned> g_wq_next{0};
+}  // namespace
+
+unsigned* attn_wq_slot() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= WQ_MAX_DEVICES) return nullptr;
+    unsigned* base;
+    {
+        std::lock_guard<std::mutex> lock(g_wq_mu);
+        if (!g_wq_base[dev]) {
+            void* p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(attn_wq_pool)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return nullptr;
+            }
+            g_wq_base[dev] = static_cast<unsigned*>(p);
+        }
+        base = g_wq_base[dev];
+    }
+    const unsigned slot = g_wq_next.fetch_add(1u, std::memory_order_relaxed) % WQ_SLOTS;
+    return base + slot * WQ_SLOT_WORDS;
+}
+
+extern "C" int attn_set_work_queue(int mode) {
+    if (mode < -1 || mode > 1) return ATTN_ERR_BAD_SHAPE;
+    g_work_queue.store(mode, std::memory_order_relaxed);
+    return ATTN_OK;
+}
 
 extern "C" int attn_set_schedule(int rows_per_wave, int head_group) {
     if (rows_per_wave != 0 && rows_per_wave != 32 && rows_per_wave != 64) return ATTN_ERR_BAD_SHAPE;

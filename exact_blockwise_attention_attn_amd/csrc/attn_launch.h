@@ -43,6 +43,21 @@ struct AttnBwdLaunch {
 int attn_sched_rows_per_wave();   // 0, 32 or 64
 int attn_sched_head_group();      // -1, 0 (one group) or n >= 1
 int attn_sched_key_groups();      // -1, 1, 2 or 4
+int attn_sched_work_queue();      // -1 (the library's choice), 0 (off) or 1 (on)
+
+// Work-queue slot of a forward launch (wq_take in attn_tile.h), in unsigned words,
+// each counter on its own 128-byte line: the claimed count of XCD x's item list at
+// WQ_STRIDE x for x < WQ_XCD, then the count of workgroups that have finished
+// claiming.  The last of those resets the slot to zero for the next launch that
+// uses it.
+constexpr int WQ_XCD = 8;
+constexpr int WQ_STRIDE = 32;
+constexpr int WQ_SLOT_WORDS = (WQ_XCD + 1) * WQ_STRIDE;
+constexpr int WQ_SLOTS = 64;
+
+// A slot of the current device's work-queue pool (wq_take in attn_tile.h), or
+// nullptr when the pool's address cannot be had (the launch then runs without it).
+unsigned* attn_wq_slot();
 
 int attn_launch_bf16(const AttnLaunch& a);
 int attn_launch_bf16_d64(const AttnLaunch& a, bool rows32, int key_groups);   // dense d = 64 (attn_fwd_bf16_d64.hip)

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_launch.h"
+
 namespace attn_tile {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -36,6 +38,46 @@ __device__ __forceinline__ void grouped_order(int id, int BH, int n_rank, int hg
     const int r = id - g * (G * n_rank);
     rank = r / gsz;
     bh = g * G + (r - rank * gsz);
+}
+
+// Work queue of one launch (an optional kernel argument).  The launch's items keep
+// the order above: item i belongs to XCD i % 8, where the dispatcher deals workgroup
+// i round robin, so all blocks of a head still share one L2.  Instead of owning item
+// blockIdx.x, a workgroup takes the next unclaimed item of its own XCD's list, and
+// once that list is empty, the next one of another XCD's.  The grid carries a few
+// extra workgroups per XCD: on an XCD that runs ahead they take over the tail of a
+// slower one's list, which a fixed item per workgroup cannot (each XCD would get
+// exactly its share of the grid, however fast it runs).  Which workgroup computes an
+// item never changes the item's result.
+// The slot layout is in attn_launch.h (WQ_*).
+
+// One lane per workgroup whose index is at least n_static (items below n_static
+// belong to the workgroup of the same index): the item this workgroup computes, or
+// -1 when every list is exhausted.  Item i of list x = i % 8 is claimed in list
+// order from n_static / 8 on (n_static a multiple of 8); total = items of the
+// launch, n_dyn = workgroups of the launch that claim.
+__device__ __forceinline__ int wq_take(unsigned* wq, int total, int n_static, int n_dyn) {
+    const int home = (int)(blockIdx.x % WQ_XCD);
+    const int j0 = n_static / WQ_XCD;
+    int item = -1;
+    for (int k = 0; k < WQ_XCD; ++k) {
+        const int x = (home + k) % WQ_XCD;
+        const int n_x = (total - x + WQ_XCD - 1) / WQ_XCD - j0;   // unclaimed-at-launch items of list x
+        if (n_x <= 0) continue;
+        const unsigned c = atomicAdd(wq + x * WQ_STRIDE, 1u);
+        if (c < (unsigned)n_x) {
+            item = (j0 + (int)c) * WQ_XCD + x;
+            break;
+        }
+    }
+    __threadfence();                                   // the claims precede the count below
+    const unsigned done = atomicAdd(wq + WQ_XCD * WQ_STRIDE, 1u);
+    if (done == (unsigned)(n_dyn - 1)) {
+        // every claiming workgroup is past its claims: the slot is clean for its next launch
+        __threadfence();
+        for (int x = 0; x <= WQ_XCD; ++x) atomicExch(wq + x * WQ_STRIDE, 0u);
+    }
+    return item;
 }
 
 // Heads per group for a kernel that streams two [N, d] bf16 tensors of a head: the

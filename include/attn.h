@@ -319,6 +319,32 @@ int attn_set_schedule(int rows_per_wave, int head_group);
  */
 int attn_set_key_groups(int key_groups);
 
+/*
+ * attn_set_work_queue - how the bf16 forward deals its (query block, head) items to
+ * workgroups, process-wide, for every later attn_fwd call (a tuning and test switch
+ * like attn_set_schedule: every setting computes the same result, bit for bit).
+ *
+ * Without the queue, workgroup i computes item i, and the dispatcher deals the
+ * workgroups to the device's 8 XCDs round robin, an equal share each, however fast
+ * each XCD runs.  With it, the first three quarters of every XCD's items stay fixed
+ * that way; the rest are claimed at run time (one atomic counter per XCD in a slot
+ * of a device array the library owns), first from the claiming workgroup's own XCD,
+ * then from the others, and the grid carries a few extra workgroups per XCD, so an
+ * XCD that runs ahead takes over the tail of a slower one (the balance of the
+ * multi-die schedule; the Mosaic long-sequence page, §3.1, asks for balanced work
+ * across devices).  A launch leaves its slot at zero when its last claiming
+ * workgroup has claimed; the library rotates over 64 slots per device, so launches
+ * share a slot only if 64 of them run at once on one device.
+ *
+ *   mode  1 (use the queue for every dense forward launch), 0 (never), or -1 for
+ *         the library's own choice (the default: unmasked and causal launches of
+ *         at least 8192 workgroups).
+ *
+ * Returns ATTN_OK, or ATTN_ERR_BAD_SHAPE for another value (then nothing changes).
+ * Safe to call from any thread; calls already enqueued keep their setting.
+ */
+int attn_set_work_queue(int mode);
+
 /* attn_strerror - static, NUL-terminated text for a status code (never NULL). */
 const char* attn_strerror(int status);
 

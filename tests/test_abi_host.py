@@ -24,7 +24,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == ["attn_bwd", "attn_bwd_check_args", "attn_check_args", "attn_fwd",
                                     "attn_fwd_block_sparse", "attn_fwd_block_sparse_check_args", "attn_fwd_kv",
                                     "attn_fwd_kv_check_args", "attn_fwd_kv_noalloc", "attn_fwd_kv_workspace_size",
-                                    "attn_set_key_groups", "attn_set_schedule", "attn_strerror", "attn_version"]
+                                    "attn_set_key_groups", "attn_set_schedule", "attn_set_work_queue", "attn_strerror", "attn_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -293,6 +293,14 @@ def test_set_key_groups_validates():
     for kg in (0, 3, 8, -2):
         assert attn.attn_set_key_groups(kg) == _lib.ATTN_ERR_BAD_SHAPE
     assert attn.attn_set_key_groups(-1) == 0
+
+
+def test_set_work_queue_validates():
+    for mode in (1, 0, -1):
+        assert attn.attn_set_work_queue(mode) == 0
+    for mode in (2, -2, 8):
+        assert attn.attn_set_work_queue(mode) == _lib.ATTN_ERR_BAD_SHAPE
+    assert attn.attn_set_work_queue(-1) == 0
 
 
 def test_noalloc_rejects_over_limit_on_the_host():
