@@ -82,7 +82,7 @@ enum attn_status {
  * calls and may be called concurrently from several host threads.
  *
  * Tile shape: bf16 calls pick 64 or 32 query rows per wave from the shape (32 for a
- * grid too small to fill the device twice or a window narrower than 4096 keys), and
+ * grid too small to fill the device twice, a window w < 2048 or a causal window w < 4096), and
  * run workgroups in groups of heads whose K and V fit in half the device's 256 MB
  * Infinity Cache.  attn_set_schedule forces either choice; neither changes a result
  * beyond the rounding of the bf16 probabilities.  When the query blocks alone
