@@ -1062,10 +1062,17 @@ struct WorkPlan {
     unsigned* wq;
     int n_static, n_dyn;
 };
-static WorkPlan work_plan(long long total, bool band) {
+static WorkPlan work_plan(long long total, bool band, hipStream_t stream) {
     WorkPlan p{total, nullptr, 0, 0};
     const int mode = attn_sched_work_queue();
     if (mode == 0 || (mode < 0 && (band || total < 8192)) || total > (1LL << 30)) return p;
+    // a launch captured into a graph keeps its slot for every replay, and replays of
+    // one graph may overlap: captured launches run without the queue
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) {
+        (void)hipGetLastError();
+        return p;
+    }
     unsigned* wq = attn_wq_slot();
     if (!wq) return p;
     const long long n_min = total / WQ_XCD;                // items of the shortest list
@@ -1085,7 +1092,8 @@ static int launch(const AttnLaunch& a) {
     const long long total = (long long)nqt * a.B * a.H;
     int hg = attn_sched_head_group();
     if (hg < 0) hg = head_group(a.N, a.d);      // K and V of a head: causal B4 H32 N16384 d128 +12%
-    const WorkPlan wp = work_plan(total, MASK == ATTN_MASK_WINDOW || MASK == ATTN_MASK_CAUSAL_WINDOW);
+    const WorkPlan wp = work_plan(total, MASK == ATTN_MASK_WINDOW || MASK == ATTN_MASK_CAUSAL_WINDOW,
+                                  (hipStream_t)a.stream);
     hipLaunchKernelGGL((fwd_kernel<D, QB, KB, MASK, false, KG>), dim3((unsigned)wp.grid), dim3(C::NT), 0,
                        (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                        (__bf16*)a.out, a.lse, a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window, SplitArgs{},

@@ -334,7 +334,9 @@ int attn_set_key_groups(int key_groups);
  * multi-die schedule; the Mosaic long-sequence page, §3.1, asks for balanced work
  * across devices).  A launch leaves its slot at zero when its last claiming
  * workgroup has claimed; the library rotates over 64 slots per device, so launches
- * share a slot only if 64 of them run at once on one device.
+ * share a slot only if 64 of them run at once on one device.  A call made while its
+ * stream is being captured into a graph runs without the queue (the captured
+ * launch would keep one slot for every replay).
  *
  *   mode  1 (use the queue for every dense forward launch), 0 (never), or -1 for
  *         the library's own choice (the default: unmasked and causal launches of

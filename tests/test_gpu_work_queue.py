@@ -88,3 +88,38 @@ def test_queue_default_at_the_library_threshold():
     assert torch.equal(o1.view(torch.int16), o0.view(torch.int16))
     assert torch.equal(l1.view(torch.int32), l0.view(torch.int32))
     assert not torch.isnan(o1).any() and not torch.isnan(l1).any()
+
+
+def test_captured_launch_runs_without_the_queue():
+    # a launch captured into a graph must not keep a queue slot for its replays: with
+    # the queue forced on, the captured forward is replayed several times (eager work
+    # and synchronisations between replays) and every replay matches the eager call
+    B, H, N, d = 2, 8, 1024, 128
+    say(f"[gpu] work-queue graph capture B{B} H{H} N{N} d{d} causal")
+    q, k, v = make_qkv(B, H, N, d, torch.bfloat16, seed=31, device="cuda")
+    scale = float(np.float32(d ** -0.5))
+    assert attn.attn_set_work_queue(1) == 0
+    try:
+        o_ref, l_ref = _fwd_nan(q, k, v, "causal", 0, scale)
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full((B, H, N), float("nan"), dtype=torch.float32, device="cuda")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            attn.fwd(q, k, v, mask="causal", scale=scale, out=out, lse=lse)   # warm-up outside capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            attn.fwd(q, k, v, mask="causal", scale=scale, out=out, lse=lse)
+        for r in range(4):
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), o_ref.view(torch.int16)), f"replay {r}: O differs"
+            assert torch.equal(lse.view(torch.int32), l_ref.view(torch.int32)), f"replay {r}: LSE differs"
+            _fwd_nan(q, k, v, "causal", 0, scale)       # eager queued work between replays
+    finally:
+        assert attn.attn_set_work_queue(-1) == 0
