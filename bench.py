@@ -61,12 +61,16 @@ KERNEL_SOURCES = {
 
 def counted_flops(B, H, N, d, mask, window=0):
     """4 B H N^2 d for no mask, half of it for causal, 4 B H d x (pairs in the band)
-    for the window |i - j| <= w."""
+    for the window |i - j| <= w and the causal window i - w <= j <= i."""
     if mask == "none":
         return 4 * B * H * N * N * d
     if mask == "causal":
         return 2 * B * H * N * N * d
     w = min(window, N - 1)
+    if mask == "causal_window":
+        return 4 * B * H * d * (N * (w + 1) - w * (w + 1) // 2)
+    if mask != "window":
+        raise ValueError(f"unknown mask {mask!r}")
     return 4 * B * H * d * (N * (2 * w + 1) - w * (w + 1))
 
 
