@@ -185,7 +185,10 @@ constexpr int min_waves_per_simd() {
     return ((D == 128 && QB == 1 && KG == 1) || (D == 64 && QB == 1 && KG > 1)) ? 2 : 1;
 }
 
-template <int D, int QB, int KB, int MASK, bool SPLIT = false, int KG = 1>
+// WQ: the workgroup order goes through the work queue (wq_take); kernels launched
+// without it compile no trace of it (its code and live values cost the register-
+// capped 32-row kernels spills).
+template <int D, int QB, int KB, int MASK, bool SPLIT = false, int KG = 1, bool WQ = false>
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256),
                           amdgpu_waves_per_eu(min_waves_per_simd<D, QB, MASK, SPLIT, KG>(), 8)))
 void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -229,12 +232,15 @@ void fwd_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
     // Workgroup order: heads in groups of hg (grouped_order), inside a group the
     // heaviest query blocks first for the causal mask.
     // With a work queue, workgroups from wq_static on claim their item (wq_take).
+    static_assert(!WQ || (!SPLIT && !BLK), "the work queue serves the dense forward");
     int id = blockIdx.x;
-    if (!SPLIT && wq != nullptr && id >= wq_static) {
-        if (tid == 0) wq_item = wq_take(wq, BH * nqt, wq_static, wq_dyn);
-        __syncthreads();
-        id = __builtin_amdgcn_readfirstlane(wq_item);
-        if (id < 0) return;                               // every item is taken (the whole workgroup)
+    if constexpr (WQ) {
+        if (id >= wq_static) {
+            if (tid == 0) wq_item = wq_take(wq, BH * nqt, wq_static, wq_dyn);
+            __syncthreads();
+            id = __builtin_amdgcn_readfirstlane(wq_item);
+            if (id < 0) return;                           // every item is taken (the whole workgroup)
+        }
     }
     int rank, bh, split = 0;
     if constexpr (SPLIT) {
@@ -1062,10 +1068,10 @@ struct WorkPlan {
     unsigned* wq;
     int n_static, n_dyn;
 };
-static WorkPlan work_plan(long long total, bool band, hipStream_t stream) {
+static WorkPlan work_plan(long long total, bool eligible, bool band, hipStream_t stream) {
     WorkPlan p{total, nullptr, 0, 0};
     const int mode = attn_sched_work_queue();
-    if (mode == 0 || (mode < 0 && (band || total < 8192)) || total > (1LL << 30)) return p;
+    if (!eligible || mode == 0 || (mode < 0 && (band || total < 8192)) || total > (1LL << 30)) return p;
     // a launch captured into a graph keeps its slot for every replay, and replays of
     // one graph may overlap: captured launches run without the queue
     hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
@@ -1092,12 +1098,23 @@ static int launch(const AttnLaunch& a) {
     const long long total = (long long)nqt * a.B * a.H;
     int hg = attn_sched_head_group();
     if (hg < 0) hg = head_group(a.N, a.d);      // K and V of a head: causal B4 H32 N16384 d128 +12%
-    const WorkPlan wp = work_plan(total, MASK == ATTN_MASK_WINDOW || MASK == ATTN_MASK_CAUSAL_WINDOW,
+    // the queue serves the 64-row kernels of the unmasked and causal forward
+    constexpr bool ELIG = QB == 2 && KG == 1 && (MASK == ATTN_MASK_NONE || MASK == ATTN_MASK_CAUSAL);
+    const WorkPlan wp = work_plan(total, ELIG, MASK == ATTN_MASK_WINDOW || MASK == ATTN_MASK_CAUSAL_WINDOW,
                                   (hipStream_t)a.stream);
-    hipLaunchKernelGGL((fwd_kernel<D, QB, KB, MASK, false, KG>), dim3((unsigned)wp.grid), dim3(C::NT), 0,
+    if constexpr (ELIG) {
+        if (wp.wq) {
+            hipLaunchKernelGGL((fwd_kernel<D, QB, KB, MASK, false, KG, true>), dim3((unsigned)wp.grid), dim3(C::NT),
+                               0, (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                               (__bf16*)a.out, a.lse, a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window,
+                               SplitArgs{}, BlockArgs{}, hg, wp.wq, wp.n_static, wp.n_dyn);
+            return 0;
+        }
+    }
+    hipLaunchKernelGGL((fwd_kernel<D, QB, KB, MASK, false, KG>), dim3((unsigned)total), dim3(C::NT), 0,
                        (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                        (__bf16*)a.out, a.lse, a.B * a.H, a.N, nqt, a.c_log2, a.negate_q, a.window, SplitArgs{},
-                       BlockArgs{}, hg, wp.wq, wp.n_static, wp.n_dyn);
+                       BlockArgs{}, hg);
     return 0;
 }
 

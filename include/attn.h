@@ -338,8 +338,9 @@ int attn_set_key_groups(int key_groups);
  * stream is being captured into a graph runs without the queue (the captured
  * launch would keep one slot for every replay).
  *
- *   mode  1 (use the queue for every dense forward launch), 0 (never), or -1 for
- *         the library's own choice (the default: unmasked and causal launches of
+ *   mode  1 (use the queue for every launch it serves: the unmasked and causal
+ *         forward at 64 query rows per wave and one key group), 0 (never), or -1
+ *         for the library's own choice (the default: those launches when they have
  *         at least 8192 workgroups).
  *
  * Returns ATTN_OK, or ATTN_ERR_BAD_SHAPE for another value (then nothing changes).
