@@ -93,10 +93,11 @@ def test_checker_ignores_value_replaced_by_mfma():
 @pytest.mark.skipif(shutil.which(_build.HIPCC) is None and not os.path.exists(_build.HIPCC), reason="hipcc not found")
 # the d = 128 kernels (4 masks x (rows per wave {32, 64}, plus the split-KV mode at 32)
 # + the two block-layout kinds + 2 dense masks x rows per wave {32, 64} x key groups
-# {2, 4}) and the d = 64 split-KV and block-layout kernels live in attn_fwd_bf16.hip;
-# the dense d = 64 kernels (4 masks x rows per wave {32, 64}, plus the 8 key-group
-# kernels) in attn_fwd_bf16_d64.hip, built with its own flags
-@pytest.mark.parametrize("src,count", [("attn_fwd_bf16.hip", 28), ("attn_fwd_bf16_d64.hip", 16)])
+# {2, 4} + the work-queue form of the 2 dense masks at 64 rows) and the d = 64
+# split-KV and block-layout kernels live in attn_fwd_bf16.hip; the dense d = 64
+# kernels (4 masks x rows per wave {32, 64}, plus the 8 key-group kernels and the 2
+# work-queue kernels) in attn_fwd_bf16_d64.hip, built with its own flags
+@pytest.mark.parametrize("src,count", [("attn_fwd_bf16.hip", 30), ("attn_fwd_bf16_d64.hip", 18)])
 def test_bf16_kernel_asm_mfma_sources_not_written_by_valu(src, count):
     with tempfile.TemporaryDirectory() as tmp:
         out = os.path.join(tmp, "k.s")
