@@ -192,10 +192,11 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
 #pragma unroll
         for (int r = 0; r < 16; ++r) { dk[j][r] = 0.f; dv[j][r] = 0.f; }
 
-    // LSE (log2 domain) and D of the tile's rows: wave 0, one row per lane
+    // LSE and D of the tile's rows: wave 0, one row per lane.  The LSE goes to the log2
+    // domain only where it is written to LDS, so nothing waits on these loads early.
     auto stage_load = [&](int t, float& l2, float& dd) __attribute__((always_inline)) {
         const int row = min(t * BT + (lane & 31), N - 1);
-        l2 = lse_h[row] * LOG2E;
+        l2 = lse_h[row];
         dd = *reinterpret_cast<const float*>(dscratch + ((size_t)bh * N + row) * D * 2);
     };
 
@@ -206,7 +207,7 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
     if (wave == 0 && lane < BT) {
         float l2, dd;
         stage_load(t_lo, l2, dd);
-        lbuf0[lane] = l2;
+        lbuf0[lane] = l2 * LOG2E;
         dbuf0[lane] = dd;
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -225,11 +226,6 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
         float* dn = B ? dbuf0 : dbuf1;
         const bool more = u + 1 < n_tiles;
         float l2n = 0.f, ddn = 0.f;
-        if (more) {
-            ld.load(qrs, t + 1, N, qn, wave);
-            ld.load(grs, t + 1, N, gn, wave);
-            if (wave == 0 && lane < BT) stage_load(t + 1, l2n, ddn);
-        }
         // S = Q_t K^T and dP = dO_t V^T: rows = the tile's queries, columns = keys (lanes)
         f32x16 s, dp;
 #pragma unroll
@@ -241,6 +237,15 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
             const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gb + o);
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[k], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[k], dp, 0, 0, 0);
+        }
+        // the next tile's loads go out after the K and V operands are used: at d = 128
+        // some of those operands are reloaded from scratch each step, and a wait for a
+        // reload issued after the tile loads (loads complete in order) would wait for
+        // the whole next tile
+        if (more) {
+            if (wave == 0 && lane < BT) stage_load(t + 1, l2n, ddn);
+            ld.load(qrs, t + 1, N, qn, wave);
+            ld.load(grs, t + 1, N, gn, wave);
         }
         // per row r of the C layout: query 8 (r/4) + 4 hl + r%4 of the tile; LSE and D
         // read four rows at a time, right before use.  At d = 64 the element mask runs only
@@ -296,7 +301,9 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
             }
         }
         if (more && wave == 0 && lane < BT) {
-            ln_[lane] = l2n;
+            // (the empty asm keeps the multiply, and so the wait for the load, here)
+            asm volatile("" : "+v"(l2n));
+            ln_[lane] = l2n * LOG2E;
             dn[lane] = ddn;
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
