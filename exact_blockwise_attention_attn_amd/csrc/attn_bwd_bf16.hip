@@ -150,6 +150,11 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
     __shared__ __attribute__((aligned(1024))) char gbuf0[TILE];
     __shared__ __attribute__((aligned(1024))) char gbuf1[TILE];
     __shared__ __attribute__((aligned(16))) float lbuf0[BT], lbuf1[BT], dbuf0[BT], dbuf1[BT];
+    // at d = 128 the last two K and V operand slabs of each lane wait in LDS (4 KB per
+    // wave) instead of registers: under the 256-register cap the compiler would
+    // otherwise reload spilled operands from scratch on every tile
+    constexpr int NL = D == 128 ? 2 : 0;               // slabs kept in LDS
+    __shared__ __attribute__((aligned(16))) bf16x8 kvl[NL ? NW * NL * 2 * 64 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -170,6 +175,13 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
     for (int s = 0; s < NS; ++s) {
         kop[s] = load_row8(K + head + (size_t)kk * D + 16 * s + 8 * hl, negate);
         vop[s] = load_row8(V + head + (size_t)kk * D + 16 * s + 8 * hl, false);
+    }
+    if constexpr (NL) {                                // each lane reads back only its own slots
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            kvl[((wave * NL + j) * 2 + 0) * 64 + lane] = kop[NS - NL + j];
+            kvl[((wave * NL + j) * 2 + 1) * 64 + lane] = vop[NS - NL + j];
+        }
     }
     int q_lo, q_hi;                                    // queries that see this key
     allowed_interval<MASK, true>(kk, N, window, q_lo, q_hi);
@@ -235,8 +247,12 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
             const int o = (k >> 1) * (4 * BT * 16) + ((k & 1) ? off.row_odd : off.row_even);
             const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + o);
             const bf16x8 ga = *reinterpret_cast<const bf16x8*>(gb + o);
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kop[k], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vop[k], dp, 0, 0, 0);
+            const bool in_lds = k >= NS - NL;
+            const int j = in_lds ? k - (NS - NL) : 0;
+            const bf16x8 kb_ = in_lds ? kvl[((wave * NL + j) * 2 + 0) * 64 + lane] : kop[k];
+            const bf16x8 vb_ = in_lds ? kvl[((wave * NL + j) * 2 + 1) * 64 + lane] : vop[k];
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb_, s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb_, dp, 0, 0, 0);
         }
         // the next tile's loads go out after the K and V operands are used: at d = 128
         // some of those operands are reloaded from scratch each step, and a wait for a
