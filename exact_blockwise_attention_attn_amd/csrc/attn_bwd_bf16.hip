@@ -238,6 +238,15 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
         float* dn = B ? dbuf0 : dbuf1;
         const bool more = u + 1 < n_tiles;
         float l2n = 0.f, ddn = 0.f;
+        // the next tile's loads go out first in the step, after wave 0's LSE and D loads:
+        // loads complete in order, so a wait for those (the compiler may place one early)
+        // then never waits for the tile as well.  Nothing else in the step reads memory
+        // (no register spills), so the tile has the whole step to arrive.
+        if (more && wave == 0 && lane < BT) stage_load(t + 1, l2n, ddn);
+        if (more) {
+            ld.load(qrs, t + 1, N, qn, wave);
+            ld.load(grs, t + 1, N, gn, wave);
+        }
         // S = Q_t K^T and dP = dO_t V^T: rows = the tile's queries, columns = keys (lanes)
         f32x16 s, dp;
 #pragma unroll
@@ -253,15 +262,6 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
             const bf16x8 vb_ = in_lds ? kvl[((wave * NL + j) * 2 + 1) * 64 + lane] : vop[k];
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb_, s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb_, dp, 0, 0, 0);
-        }
-        // the next tile's loads go out after the K and V operands are used: at d = 128
-        // some of those operands are reloaded from scratch each step, and a wait for a
-        // reload issued after the tile loads (loads complete in order) would wait for
-        // the whole next tile
-        if (more) {
-            if (wave == 0 && lane < BT) stage_load(t + 1, l2n, ddn);
-            ld.load(qrs, t + 1, N, qn, wave);
-            ld.load(grs, t + 1, N, gn, wave);
         }
         // per row r of the C layout: query 8 (r/4) + 4 hl + r%4 of the tile; LSE and D
         // read four rows at a time, right before use.  At d = 64 the element mask runs only
