@@ -150,10 +150,11 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
     __shared__ __attribute__((aligned(1024))) char gbuf0[TILE];
     __shared__ __attribute__((aligned(1024))) char gbuf1[TILE];
     __shared__ __attribute__((aligned(16))) float lbuf0[BT], lbuf1[BT], dbuf0[BT], dbuf1[BT];
-    // at d = 128 the last two K and V operand slabs of each lane wait in LDS (4 KB per
-    // wave) instead of registers: under the 256-register cap the compiler would
-    // otherwise reload spilled operands from scratch on every tile
-    constexpr int NL = D == 128 ? 2 : 0;               // slabs kept in LDS
+    // at d = 128 the last four of the eight K and V operand slabs of each lane wait in
+    // LDS (8 KB per wave) instead of registers: under the 256-register cap the compiler
+    // would otherwise reload spilled operands from scratch on every tile, and the
+    // unmasked copy of the probability block below would not fit
+    constexpr int NL = D == 128 ? 4 : 0;               // slabs kept in LDS
     __shared__ __attribute__((aligned(16))) bf16x8 kvl[NL ? NW * NL * 2 * 64 : 1];
 
     const int tid = threadIdx.x;
@@ -264,8 +265,8 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vb_, dp, 0, 0, 0);
         }
         // per row r of the C layout: query 8 (r/4) + 4 hl + r%4 of the tile; LSE and D
-        // read four rows at a time, right before use.  At d = 64 the element mask runs only
-        // when the tile's queries are not all allowed for every key of the wave.
+        // read four rows at a time, right before use.  The element mask runs only when the
+        // tile's queries are not all allowed for every key of the wave.
         bf16x8 pp[2], dsp[2];
         const int rel0 = t * BT + 4 * hl - q_lo;
         auto probs = [&](auto masked) __attribute__((always_inline)) {
@@ -287,11 +288,7 @@ void dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, con
                 }
             }
         };
-        // (at d = 128 the second copy of this block costs the register-capped kernel
-        // spills: there the mask runs on every tile)
-        if constexpr (D == 128) {
-            probs(IntC<1>{});
-        } else {
+        {
             const int a0 = t * BT - q_lo;              // the whole tile inside this key's queries?
             if (__any(!(a0 >= 0 && a0 + (BT - 1) <= (int)q_span))) {
                 asm volatile("" ::: "memory");
